@@ -1,0 +1,435 @@
+/*
+ * ccl_oracle.c -- plain, slow, obviously-correct CPU oracle for the collective
+ * data plane.  TEST INFRASTRUCTURE ONLY: it is built and called by the test
+ * suite, by the smoke check and by the bench's cpu_baseline leg, never by the
+ * product library, and it shares no source, header, table or helper with it.
+ *
+ * Sources (the web pages this project is built from):
+ *   [digest]  "NCCL M2N vs T-CCL" digest, lqnn.cn news 207677:
+ *             s1.2 (layout-derived traffic, leader balance), s1.3 (Mesh /
+ *             Shard / Replicate descriptors and their constraints), s1.4
+ *             (Example A: TP4 -> TP2 x DP2, Example B: per-PP-stage reshard),
+ *             s2.1 (add/min/max reduction op set), s2.2 (owner-local shard-in
+ *             reduction, load-once shard-out), s2.3 (P shards for P ranks,
+ *             NCCL-aligned collective semantics), s2.5 (all-reduce = shard-in
+ *             followed by shard-out).
+ *   [roadmap] "nccl-extensions" page (NCCL roadmap explainer), GENK section:
+ *             ring all-reduce / reduce-scatter / all-gather semantics.
+ *
+ * Readings the pages leave open (each also listed in the design notes):
+ *   - Reduction is a fold in rank order 0..P-1 that starts from rank 0's
+ *     value, accumulates in fp32 (int32 wraps), and narrows once at the end.
+ *   - bf16 narrowing is round-to-nearest-even; a NaN becomes 0x7FC0.
+ *   - min keeps the earlier operand unless the later one is strictly smaller;
+ *     max likewise with strictly greater (so ties, including +0/-0, keep the
+ *     earlier rank's value).
+ *   - Mesh ranks are numbered row-major (last mesh axis fastest) from
+ *     start_rank; placements[k] applies to mesh axis k (both pinned by
+ *     Example A in [digest] s1.4).
+ *   - Shard(d) over m parts splits dim d into m equal contiguous blocks and
+ *     requires m to divide the dim.
+ *
+ * Every function returns 0 on success and a negative value on bad input.
+ * Style: scalar loops, no SIMD intrinsics, no threads, no fast-math.
+ */
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+/* The oracle's own type and op codes (the Python wrapper maps names to these). */
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_I32 2
+#define ORC_SUM 0
+#define ORC_MIN 1
+#define ORC_MAX 2
+
+#define ORC_MAX_MESH_DIMS 8
+#define ORC_MAX_TENSOR_DIMS 8
+
+/* ---------------------------------------------------------------- scalars */
+
+static float bits_to_f32(uint32_t u) {
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static uint32_t f32_to_bits(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return u;
+}
+
+/* bf16 -> fp32 is exact: the bf16 pattern is the top half of the fp32 one. */
+static float orc_bf16_widen(uint16_t h) { return bits_to_f32((uint32_t)h << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even. */
+static uint16_t orc_bf16_narrow(float f) {
+    uint32_t u = f32_to_bits(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0u; /* NaN */
+    uint32_t lsb = (u >> 16) & 1u;
+    u = u + 0x7fffu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static int dtype_size(int dtype) {
+    switch (dtype) {
+    case ORC_F32: return 4;
+    case ORC_BF16: return 2;
+    case ORC_I32: return 4;
+    default: return 0;
+    }
+}
+
+static float fold_f32(float acc, float v, int op) {
+    if (op == ORC_SUM) return acc + v;
+    if (op == ORC_MIN) return (v < acc) ? v : acc;
+    return (v > acc) ? v : acc;
+}
+
+static int32_t fold_i32(int32_t acc, int32_t v, int op) {
+    if (op == ORC_SUM) return (int32_t)((uint32_t)acc + (uint32_t)v); /* wraps */
+    if (op == ORC_MIN) return (v < acc) ? v : acc;
+    return (v > acc) ? v : acc;
+}
+
+/*
+ * The reduction of element i over the P rank buffers, written to dst
+ * (one element of the given dtype).  Shard-in per [digest] s2.2: the owner
+ * takes every rank's contribution and reduces it locally; the op set is the
+ * one [digest] s2.1 lists (add, min, max).
+ */
+static void fold_element(const void *const *x, int P, int dtype, int op, size_t i, void *dst) {
+    if (dtype == ORC_I32) {
+        int32_t acc;
+        memcpy(&acc, (const char *)x[0] + i * 4, 4);
+        for (int r = 1; r < P; ++r) {
+            int32_t v;
+            memcpy(&v, (const char *)x[r] + i * 4, 4);
+            acc = fold_i32(acc, v, op);
+        }
+        memcpy(dst, &acc, 4);
+    } else if (dtype == ORC_F32) {
+        float acc;
+        memcpy(&acc, (const char *)x[0] + i * 4, 4);
+        for (int r = 1; r < P; ++r) {
+            float v;
+            memcpy(&v, (const char *)x[r] + i * 4, 4);
+            acc = fold_f32(acc, v, op);
+        }
+        memcpy(dst, &acc, 4);
+    } else {
+        uint16_t h;
+        memcpy(&h, (const char *)x[0] + i * 2, 2);
+        float acc = orc_bf16_widen(h);
+        for (int r = 1; r < P; ++r) {
+            memcpy(&h, (const char *)x[r] + i * 2, 2);
+            acc = fold_f32(acc, orc_bf16_widen(h), op);
+        }
+        h = orc_bf16_narrow(acc);
+        memcpy(dst, &h, 2);
+    }
+}
+
+static int check_common(const void *const *send, int P, int dtype, int op) {
+    if (!send || P < 1 || dtype_size(dtype) == 0) return -1;
+    if (op != ORC_SUM && op != ORC_MIN && op != ORC_MAX) return -1;
+    return 0;
+}
+
+/* --------------------------------------------------------- collectives */
+
+/*
+ * All-reduce: every output buffer q receives, at every index i, the rank-order
+ * fold of the P inputs at i.  [digest] s2.5 defines all-reduce as shard-in
+ * followed by shard-out, so each of the P outputs holds the same reduced value.
+ */
+int orc_all_reduce(const void *const *send, void *const *recv, int P, size_t count, int dtype,
+                   int op) {
+    if (check_common(send, P, dtype, op) || !recv) return -1;
+    const int s = dtype_size(dtype);
+    char tmp[8];
+    for (size_t i = 0; i < count; ++i) {
+        fold_element(send, P, dtype, op, i, tmp);
+        for (int q = 0; q < P; ++q) memcpy((char *)recv[q] + i * s, tmp, s);
+    }
+    return 0;
+}
+
+/*
+ * Reduce-scatter: rank s keeps the reduction of shard s, i.e. input elements
+ * [s*M, (s+1)*M) with M = recvcount ([digest] s2.3: the logical tensor is cut
+ * into P shards, one per rank; s2.2: the owner reduces its shard locally).
+ */
+int orc_reduce_scatter(const void *const *send, void *const *recv, int P, size_t recvcount,
+                       int dtype, int op) {
+    if (check_common(send, P, dtype, op) || !recv) return -1;
+    const int s = dtype_size(dtype);
+    for (int sh = 0; sh < P; ++sh)
+        for (size_t j = 0; j < recvcount; ++j)
+            fold_element(send, P, dtype, op, (size_t)sh * recvcount + j,
+                         (char *)recv[sh] + j * s);
+    return 0;
+}
+
+/*
+ * All-gather: every output q holds all shards in rank order, shard r at
+ * element offset r*M ([digest] s2.2 shard-out: the owner's shard goes to every
+ * peer).
+ */
+int orc_all_gather(const void *const *send, void *const *recv, int P, size_t sendcount,
+                   int dtype) {
+    if (!send || !recv || P < 1 || dtype_size(dtype) == 0) return -1;
+    const size_t s = (size_t)dtype_size(dtype);
+    for (int q = 0; q < P; ++q)
+        for (int r = 0; r < P; ++r)
+            for (size_t j = 0; j < sendcount; ++j)
+                memcpy((char *)recv[q] + ((size_t)r * sendcount + j) * s,
+                       (const char *)send[r] + j * s, s);
+    return 0;
+}
+
+/* The fold at selected indices only: out[k] = fold(idx[k]).  Lets a test check
+ * outputs of buffers far too large for the full oracle. */
+int orc_fold_at(const void *const *send, int P, int dtype, int op, const uint64_t *idx, size_t n,
+                void *out) {
+    if (check_common(send, P, dtype, op) || (n && (!idx || !out))) return -1;
+    const int s = dtype_size(dtype);
+    for (size_t k = 0; k < n; ++k) fold_element(send, P, dtype, op, (size_t)idx[k], (char *)out + k * s);
+    return 0;
+}
+
+/* ------------------------------------------------------------- reshard */
+
+/* A layout: a mesh of ranks plus one placement per mesh axis ([digest] s1.3). */
+typedef struct {
+    int ndims;
+    int64_t dims[ORC_MAX_MESH_DIMS];
+    int64_t start_rank;
+    int kind[ORC_MAX_MESH_DIMS]; /* 0 = Replicate, 1 = Shard */
+    int sdim[ORC_MAX_MESH_DIMS]; /* tensor dim for Shard */
+} orc_layout;
+
+static int64_t layout_size(const orc_layout *L) {
+    int64_t n = 1;
+    for (int k = 0; k < L->ndims; ++k) n *= L->dims[k];
+    return n;
+}
+
+static int layout_check(const orc_layout *L, int ndim, const int64_t *shape) {
+    if (L->ndims < 1 || L->ndims > ORC_MAX_MESH_DIMS || L->start_rank < 0) return -1;
+    for (int k = 0; k < L->ndims; ++k) {
+        if (L->dims[k] < 1) return -1;
+        if (L->kind[k] == 1) {
+            int d = L->sdim[k];
+            if (d < 0 || d >= ndim) return -1;
+            if (shape[d] % L->dims[k] != 0) return -2; /* uneven split */
+            for (int k2 = 0; k2 < k; ++k2)
+                if (L->kind[k2] == 1 && L->sdim[k2] == d) return -1; /* same dim twice */
+        } else if (L->kind[k] != 0) {
+            return -1;
+        }
+    }
+    return 0;
+}
+
+/* Mesh coordinate of the l-th rank of the mesh: row-major, last axis fastest. */
+static void unravel_mesh(const orc_layout *L, int64_t l, int64_t *c) {
+    for (int k = L->ndims - 1; k >= 0; --k) {
+        c[k] = l % L->dims[k];
+        l /= L->dims[k];
+    }
+}
+
+/* The index box [lo, hi) a mesh coordinate holds: Shard(d) on axis k cuts dim d
+ * into dims[k] equal blocks and takes block c[k]; Replicate leaves it whole. */
+static void rank_box(const orc_layout *L, const int64_t *c, int ndim, const int64_t *shape,
+                     int64_t *lo, int64_t *hi) {
+    for (int d = 0; d < ndim; ++d) {
+        lo[d] = 0;
+        hi[d] = shape[d];
+    }
+    for (int k = 0; k < L->ndims; ++k) {
+        if (L->kind[k] != 1) continue;
+        int d = L->sdim[k];
+        int64_t part = shape[d] / L->dims[k];
+        lo[d] = c[k] * part;
+        hi[d] = lo[d] + part;
+    }
+}
+
+static int box_contains(const int64_t *lo, const int64_t *hi, const int64_t *g, int ndim) {
+    for (int d = 0; d < ndim; ++d)
+        if (g[d] < lo[d] || g[d] >= hi[d]) return 0;
+    return 1;
+}
+
+/* Row-major offset of g inside the box. */
+static int64_t box_offset(const int64_t *lo, const int64_t *hi, const int64_t *g, int ndim) {
+    int64_t off = 0;
+    for (int d = 0; d < ndim; ++d) off = off * (hi[d] - lo[d]) + (g[d] - lo[d]);
+    return off;
+}
+
+static int fill_layout(orc_layout *L, int ndims, const int64_t *dims, int64_t start,
+                       const int *kind, const int *sdim) {
+    if (ndims < 1 || ndims > ORC_MAX_MESH_DIMS || !dims || !kind || !sdim) return -1;
+    L->ndims = ndims;
+    L->start_rank = start;
+    for (int k = 0; k < ndims; ++k) {
+        L->dims[k] = dims[k];
+        L->kind[k] = kind[k];
+        L->sdim[k] = sdim[k];
+    }
+    return 0;
+}
+
+static int meshes_disjoint(const orc_layout *A, const orc_layout *B) {
+    int64_t a0 = A->start_rank, a1 = a0 + layout_size(A);
+    int64_t b0 = B->start_rank, b1 = b0 + layout_size(B);
+    return a1 <= b0 || b1 <= a0;
+}
+
+/*
+ * Reshard by brute force, one element at a time ([digest] s1.2: only the bytes
+ * the destination layout needs are moved; s1.3: layouts are (mesh, placement)
+ * pairs; the two meshes must be disjoint).
+ *
+ * For every global index g: the source ranks whose box contains g all hold the
+ * same value (checked); the value is taken from the lowest such rank and
+ * written into every destination rank whose box contains g, at g's row-major
+ * offset inside that rank's box.  src_bufs[l] / dst_bufs[l] belong to the l-th
+ * rank of the respective mesh.  Returns -3 if source replicas disagree and -4
+ * if some destination element is not covered.
+ */
+int orc_reshard(int ndim, const int64_t *shape, int elem_size,
+                int s_ndims, const int64_t *s_dims, int64_t s_start, const int *s_kind,
+                const int *s_sdim,
+                int d_ndims, const int64_t *d_dims, int64_t d_start, const int *d_kind,
+                const int *d_sdim,
+                const void *const *src_bufs, void *const *dst_bufs) {
+    orc_layout S, D;
+    if (ndim < 1 || ndim > ORC_MAX_TENSOR_DIMS || !shape || elem_size < 1 || elem_size > 16)
+        return -1;
+    for (int d = 0; d < ndim; ++d)
+        if (shape[d] < 0) return -1;
+    if (fill_layout(&S, s_ndims, s_dims, s_start, s_kind, s_sdim)) return -1;
+    if (fill_layout(&D, d_ndims, d_dims, d_start, d_kind, d_sdim)) return -1;
+    int rc;
+    if ((rc = layout_check(&S, ndim, shape))) return rc;
+    if ((rc = layout_check(&D, ndim, shape))) return rc;
+    if (!meshes_disjoint(&S, &D)) return -1;
+    if (!src_bufs || !dst_bufs) return -1;
+
+    int64_t numel = 1;
+    for (int d = 0; d < ndim; ++d) numel *= shape[d];
+    const int64_t ns = layout_size(&S), nd = layout_size(&D);
+    int64_t g[ORC_MAX_TENSOR_DIMS], c[ORC_MAX_MESH_DIMS];
+    int64_t lo[ORC_MAX_TENSOR_DIMS], hi[ORC_MAX_TENSOR_DIMS];
+
+    for (int64_t flat = 0; flat < numel; ++flat) {
+        int64_t t = flat;
+        for (int d = ndim - 1; d >= 0; --d) {
+            g[d] = t % shape[d];
+            t /= shape[d];
+        }
+        const unsigned char *val = NULL;
+        for (int64_t l = 0; l < ns; ++l) {
+            unravel_mesh(&S, l, c);
+            rank_box(&S, c, ndim, shape, lo, hi);
+            if (!box_contains(lo, hi, g, ndim)) continue;
+            const unsigned char *p =
+                (const unsigned char *)src_bufs[l] + box_offset(lo, hi, g, ndim) * elem_size;
+            if (!val)
+                val = p;
+            else if (memcmp(val, p, (size_t)elem_size) != 0)
+                return -3;
+        }
+        if (!val) return -4; /* cannot happen for a valid layout */
+        int written = 0;
+        for (int64_t l = 0; l < nd; ++l) {
+            unravel_mesh(&D, l, c);
+            rank_box(&D, c, ndim, shape, lo, hi);
+            if (!box_contains(lo, hi, g, ndim)) continue;
+            memcpy((unsigned char *)dst_bufs[l] + box_offset(lo, hi, g, ndim) * elem_size, val,
+                   (size_t)elem_size);
+            ++written;
+        }
+        if (!written) return -4;
+    }
+    return 0;
+}
+
+/*
+ * Point query of the same reshard: for destination rank dst_l (its index in
+ * the destination mesh) and element offsets local[k] inside its buffer, write
+ * the value that rank must end up holding.  The offset is mapped back to its
+ * global index through the rank's box, and the value is read from the lowest
+ * source rank whose box holds that index.
+ */
+int orc_reshard_at(int ndim, const int64_t *shape, int elem_size,
+                   int s_ndims, const int64_t *s_dims, int64_t s_start, const int *s_kind,
+                   const int *s_sdim,
+                   int d_ndims, const int64_t *d_dims, int64_t d_start, const int *d_kind,
+                   const int *d_sdim,
+                   const void *const *src_bufs, int64_t dst_l, const uint64_t *local, size_t n,
+                   void *out) {
+    orc_layout S, D;
+    if (ndim < 1 || ndim > ORC_MAX_TENSOR_DIMS || !shape || elem_size < 1 || elem_size > 16)
+        return -1;
+    if (fill_layout(&S, s_ndims, s_dims, s_start, s_kind, s_sdim)) return -1;
+    if (fill_layout(&D, d_ndims, d_dims, d_start, d_kind, d_sdim)) return -1;
+    int rc;
+    if ((rc = layout_check(&S, ndim, shape))) return rc;
+    if ((rc = layout_check(&D, ndim, shape))) return rc;
+    if (dst_l < 0 || dst_l >= layout_size(&D) || !src_bufs || (n && (!local || !out))) return -1;
+
+    int64_t c[ORC_MAX_MESH_DIMS], lo[ORC_MAX_TENSOR_DIMS], hi[ORC_MAX_TENSOR_DIMS];
+    int64_t dlo[ORC_MAX_TENSOR_DIMS], dhi[ORC_MAX_TENSOR_DIMS], g[ORC_MAX_TENSOR_DIMS];
+    unravel_mesh(&D, dst_l, c);
+    rank_box(&D, c, ndim, shape, dlo, dhi);
+    int64_t local_numel = 1;
+    for (int d = 0; d < ndim; ++d) local_numel *= dhi[d] - dlo[d];
+    const int64_t ns = layout_size(&S);
+
+    for (size_t k = 0; k < n; ++k) {
+        if ((int64_t)local[k] >= local_numel) return -1;
+        int64_t t = (int64_t)local[k];
+        for (int d = ndim - 1; d >= 0; --d) {
+            int64_t ext = dhi[d] - dlo[d];
+            g[d] = dlo[d] + t % ext;
+            t /= ext;
+        }
+        int found = 0;
+        for (int64_t l = 0; l < ns && !found; ++l) {
+            unravel_mesh(&S, l, c);
+            rank_box(&S, c, ndim, shape, lo, hi);
+            if (!box_contains(lo, hi, g, ndim)) continue;
+            memcpy((unsigned char *)out + k * (size_t)elem_size,
+                   (const unsigned char *)src_bufs[l] + box_offset(lo, hi, g, ndim) * elem_size,
+                   (size_t)elem_size);
+            found = 1;
+        }
+        if (!found) return -4;
+    }
+    return 0;
+}
+
+/* Number of elements a rank of a layout holds (its box volume). */
+int64_t orc_local_numel(int ndim, const int64_t *shape, int m_ndims, const int64_t *m_dims,
+                        const int *kind, const int *sdim) {
+    orc_layout L;
+    if (ndim < 1 || ndim > ORC_MAX_TENSOR_DIMS || !shape) return -1;
+    if (fill_layout(&L, m_ndims, m_dims, 0, kind, sdim)) return -1;
+    if (layout_check(&L, ndim, shape)) return -1;
+    int64_t c[ORC_MAX_MESH_DIMS] = {0}, lo[ORC_MAX_TENSOR_DIMS], hi[ORC_MAX_TENSOR_DIMS];
+    rank_box(&L, c, ndim, shape, lo, hi);
+    int64_t n = 1;
+    for (int d = 0; d < ndim; ++d) n *= hi[d] - lo[d];
+    return n;
+}
+
+/* Exposed for tests of the rounding rule itself. */
+uint16_t orc_narrow_bf16(float f) { return orc_bf16_narrow(f); }
+float orc_widen_bf16(uint16_t h) { return orc_bf16_widen(h); }

@@ -1,0 +1,82 @@
+"""Seeded synthetic rank buffers, shared by the tests, the smoke check and the bench.
+
+This module only draws numbers: it holds none of the collectives' arithmetic.
+Every draw uses numpy's PCG64 ``default_rng(seed)``; rank r's buffer is the
+r-th draw of N values from one generator (rank-major order).  bf16 buffers are
+fp32 draws converted by PyTorch's CPU ``to(torch.bfloat16)`` (round to nearest
+even) and returned as uint16 bit patterns.
+
+Distributions (the workloads the reduce/copy data plane is measured on):
+  ``uniform``  2*U - 1 with U ~ U[0,1) in float32, i.e. values in [-1, 1)
+  ``normal``   standard normal, float32
+  ``w002``     0.02 * standard normal (weight-like tensors for reshard)
+  ``int20``    integers uniform in [-2**20, 2**20], int32
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NP_TYPES = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 array -> uint16 bf16 bit patterns (PyTorch's RNE conversion)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(h: np.ndarray) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float32 values (PyTorch's widening)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(h, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).float().numpy()
+
+
+def _draw(rng: np.random.Generator, dist: str, n: int, dtype: str) -> np.ndarray:
+    if dist == "int20":
+        if dtype != "i32":
+            raise ValueError("int20 draws are int32")
+        return rng.integers(-(2**20), 2**20, size=n, dtype=np.int32, endpoint=True)
+    if dist == "uniform":
+        x = rng.random(n, dtype=np.float32)
+        x *= np.float32(2.0)
+        x -= np.float32(1.0)
+    elif dist == "normal":
+        x = rng.standard_normal(n, dtype=np.float32)
+    elif dist == "w002":
+        x = rng.standard_normal(n, dtype=np.float32)
+        x *= np.float32(0.02)
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    if dtype == "i32":
+        raise ValueError("float draws cannot fill int32 buffers")
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def rank_buffers(P: int, n: int, dtype: str, dist: str, seed: int = 0) -> list[np.ndarray]:
+    """P buffers of n elements; buffer r is the r-th draw from default_rng(seed)."""
+    rng = np.random.default_rng(seed)
+    return [_draw(rng, dist, n, dtype) for _ in range(P)]
+
+
+def tensor(shape, dtype: str, dist: str, seed: int = 0) -> np.ndarray:
+    """One global tensor of the given shape (row-major), drawn like one rank buffer."""
+    rng = np.random.default_rng(seed)
+    return _draw(rng, dist, int(np.prod(shape)), dtype).reshape(shape)
+
+
+def sample_indices(n: int, k: int, seed: int = 1) -> np.ndarray:
+    """k distinct-ish sorted indices in [0, n) plus both ends, for sampled checks."""
+    if n <= 0:
+        return np.zeros(0, np.uint64)
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, n, size=min(k, n), dtype=np.int64)
+    idx = np.unique(np.concatenate([idx, [0, n - 1]]))
+    return idx.astype(np.uint64)

@@ -1,0 +1,381 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU needed).
+
+Each test ties an oracle function to something other than the oracle itself:
+independent numpy / PyTorch library routines, closed forms, the textbook
+error bound of recursive summation, invariants the pages state (all-reduce =
+reduce-scatter then all-gather; every replica identical), and the worked
+examples of the M2N/T-CCL digest (lqnn.cn news 207677) s1.4 kept under
+tests/golden/.
+"""
+from __future__ import annotations
+
+import itertools
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from _golden import load_example
+
+PS = [1, 2, 3, 4, 8]
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def bits_f32(u: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", u))[0]
+
+
+# ------------------------------------------------------------- bf16 rounding
+
+@pytest.mark.parametrize(
+    "f32_pattern, bf16_pattern",
+    [
+        (0x3F800000, 0x3F80),  # 1.0 exact
+        (0x3F808000, 0x3F80),  # halfway, even below -> stays
+        (0x3F818000, 0x3F82),  # halfway, odd below -> rounds up to even
+        (0x3F808001, 0x3F81),  # just above halfway -> up
+        (0x3F807FFF, 0x3F80),  # just below halfway -> down
+        (0xBF818000, 0xBF82),  # negative halfway, odd -> away from zero to even
+        (0x7F7FFFFF, 0x7F80),  # largest finite fp32 rounds to +inf
+        (0x7F800000, 0x7F80),  # +inf
+        (0xFF800000, 0xFF80),  # -inf
+        (0x00000001, 0x0000),  # smallest denormal rounds to +0
+        (0x00008000, 0x0000),  # denormal halfway, even -> 0
+        (0x00018000, 0x0002),  # denormal halfway, odd -> up
+        (0x80000000, 0x8000),  # -0 keeps its sign
+        (0x7FC00001, 0x7FC0),  # NaN -> canonical quiet NaN
+    ],
+)
+def test_bf16_rne_hand_worked(f32_pattern, bf16_pattern):
+    assert oracle.narrow_bf16(bits_f32(f32_pattern)) == bf16_pattern
+
+
+def test_bf16_narrow_matches_torch_rne():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[~np.isnan(x)]
+    want = si.to_bf16_bits(x)
+    got = np.array([oracle.narrow_bf16(float(v)) for v in x[:20000]], np.uint16)
+    np.testing.assert_array_equal(got, want[:20000])
+
+
+def test_bf16_widen_is_exact():
+    h = np.arange(0, 2**16, 257, dtype=np.uint16)
+    h = h[~np.isnan(si.bf16_bits_to_f32(h))]
+    want = si.bf16_bits_to_f32(h)
+    got = np.array([oracle.widen_bf16(int(v)) for v in h], np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# -------------------------------------------------------------- reductions
+
+def seq_sum_f32(xs):
+    """Independent fp32 reference: numpy elementwise IEEE adds in rank order."""
+    acc = xs[0].astype(np.float32).copy()
+    for x in xs[1:]:
+        acc = np.add(acc, x.astype(np.float32), dtype=np.float32)
+    return acc
+
+
+@pytest.mark.parametrize("P", PS)
+@pytest.mark.parametrize("n", [0, 1, 37, 4099])
+def test_allreduce_f32_sum_equals_sequential_numpy(P, n):
+    xs = si.rank_buffers(P, n, "f32", "uniform", seed=P * 100 + n)
+    ys = oracle.all_reduce(xs, "f32", "sum")
+    want = seq_sum_f32(xs)
+    for y in ys:
+        np.testing.assert_array_equal(y.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("P", PS)
+def test_allreduce_bf16_sum_equals_fp32_fold_then_torch_rne(P):
+    xs = si.rank_buffers(P, 5000, "bf16", "normal", seed=P)
+    ys = oracle.all_reduce(xs, "bf16", "sum")
+    want = si.to_bf16_bits(seq_sum_f32([si.bf16_bits_to_f32(x) for x in xs]))
+    for y in ys:
+        np.testing.assert_array_equal(y, want)
+
+
+@pytest.mark.parametrize("P", PS)
+def test_allreduce_i32_sum_exact_and_wrapping(P):
+    rng = np.random.default_rng(P)
+    xs = si.rank_buffers(P, 3001, "i32", "int20", seed=P)
+    # plus a block of huge values that must wrap in two's complement
+    big = rng.integers(-(2**31), 2**31, size=(P, 64), dtype=np.int64).astype(np.int32)
+    xs = [np.concatenate([x, b]) for x, b in zip(xs, big)]
+    ys = oracle.all_reduce(xs, "i32", "sum")
+    want = (np.sum(np.stack(xs).astype(np.int64), axis=0) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    for y in ys:
+        np.testing.assert_array_equal(y, want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", ["min", "max"])
+@pytest.mark.parametrize("P", PS)
+def test_allreduce_minmax_equals_numpy_reduce(dtype, op, P):
+    dist = "int20" if dtype == "i32" else "uniform"
+    xs = si.rank_buffers(P, 2049, dtype, dist, seed=11 * P)
+    ys = oracle.all_reduce(xs, dtype, op)
+    fn = np.minimum if op == "min" else np.maximum
+    if dtype == "bf16":
+        want = si.to_bf16_bits(fn.reduce([si.bf16_bits_to_f32(x) for x in xs]))
+    else:
+        want = fn.reduce(xs)
+    for y in ys:
+        np.testing.assert_array_equal(y, want)
+
+
+def test_minmax_ties_keep_earlier_rank_signed_zero():
+    pz, nz = np.float32(0.0), np.float32(-0.0)
+    for op in ("min", "max"):
+        y = oracle.all_reduce([np.array([pz, nz]), np.array([nz, pz])], "f32", op)[0]
+        # rank 0's zero survives in both columns
+        assert y.view(np.uint32).tolist() == [0x00000000, 0x80000000]
+
+
+@pytest.mark.parametrize("P", [2, 3, 5, 8])
+def test_fp32_fold_within_recursive_summation_bound(P):
+    """|fl(sum) - sum| <= gamma_{P-1} * sum|x| (recursive summation, u = 2^-24)."""
+    xs = si.rank_buffers(P, 20000, "f32", "normal", seed=3 * P)
+    got = oracle.all_reduce(xs, "f32", "sum")[0].astype(np.float64)
+    X = np.stack(xs).astype(np.float64)
+    exact = np.sum(X, axis=0)
+    u = 2.0 ** -24
+    gamma = (P - 1) * u / (1 - (P - 1) * u)
+    bound = gamma * np.sum(np.abs(X), axis=0)
+    assert np.all(np.abs(got - exact) <= bound)
+    # and a dropped term would be far outside it
+    assert np.any(np.abs(got - (exact - X[-1])) > bound)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_equal_inputs_sum_to_P_times_x(P, dtype):
+    """With 8-bit significands every partial sum r*x (r <= 8) is exact in fp32,
+    so the fold of P equal buffers is exactly P*x; bf16 output of a power-of-two
+    P is exact too."""
+    h = si.rank_buffers(1, 1000, "bf16", "uniform", seed=5)[0]
+    x = si.bf16_bits_to_f32(h)
+    if dtype == "f32":
+        y = oracle.all_reduce([x] * P, "f32", "sum")[0]
+        np.testing.assert_array_equal(y, x * np.float32(P))
+    else:
+        y = oracle.all_reduce([h] * P, "bf16", "sum")[0]
+        np.testing.assert_array_equal(y, si.to_bf16_bits(x * np.float32(P)))
+        if P & (P - 1) == 0:
+            np.testing.assert_array_equal(si.bf16_bits_to_f32(y), x * np.float32(P))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+def test_single_rank_is_identity(dtype):
+    dist = "int20" if dtype == "i32" else "normal"
+    x = si.rank_buffers(1, 777, dtype, dist)[0]
+    for op in ("sum", "min", "max"):
+        np.testing.assert_array_equal(oracle.all_reduce([x], dtype, op)[0], x)
+
+
+@pytest.mark.parametrize("op", ["min", "max"])
+def test_minmax_rank_permutation_invariant(op):
+    xs = si.rank_buffers(5, 999, "f32", "uniform", seed=9)
+    base = oracle.all_reduce(xs, "f32", op)[0]
+    for perm in [(4, 3, 2, 1, 0), (2, 0, 4, 1, 3)]:
+        np.testing.assert_array_equal(oracle.all_reduce([xs[i] for i in perm], "f32", op)[0], base)
+
+
+# ---------------------------------------- reduce-scatter / all-gather / fold_at
+
+@pytest.mark.parametrize("P", PS)
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("bf16", "sum"), ("i32", "sum"),
+                                      ("bf16", "max"), ("f32", "min")])
+def test_reduce_scatter_then_all_gather_is_all_reduce(P, dtype, op):
+    dist = "int20" if dtype == "i32" else "uniform"
+    xs = si.rank_buffers(P, P * 513, dtype, dist, seed=P + 1)
+    rs = oracle.reduce_scatter(xs, dtype, op)
+    ag = oracle.all_gather(rs, dtype)
+    ar = oracle.all_reduce(xs, dtype, op)
+    for q in range(P):
+        np.testing.assert_array_equal(ag[q], ar[q])
+        np.testing.assert_array_equal(ar[q], ar[0])  # replicas identical
+
+
+@pytest.mark.parametrize("P", PS)
+def test_reduce_scatter_shard_s_is_slice_of_numpy_sum(P):
+    xs = si.rank_buffers(P, P * 300, "f32", "uniform", seed=21)
+    rs = oracle.reduce_scatter(xs, "f32", "sum")
+    full = seq_sum_f32(xs)
+    for s in range(P):
+        np.testing.assert_array_equal(rs[s], np.split(full, P)[s])
+
+
+@pytest.mark.parametrize("P", PS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+def test_all_gather_is_concatenation(P, dtype):
+    dist = "int20" if dtype == "i32" else "normal"
+    xs = si.rank_buffers(P, 301, dtype, dist, seed=4)
+    ag = oracle.all_gather(xs, dtype)
+    want = np.concatenate(xs)
+    for y in ag:
+        np.testing.assert_array_equal(y, want)
+
+
+@pytest.mark.parametrize("dtype,op", [("bf16", "sum"), ("f32", "max"), ("i32", "sum")])
+def test_fold_at_equals_full_allreduce(dtype, op):
+    dist = "int20" if dtype == "i32" else "uniform"
+    xs = si.rank_buffers(8, 10007, dtype, dist, seed=2)
+    idx = si.sample_indices(10007, 500)
+    np.testing.assert_array_equal(oracle.fold_at(xs, dtype, op, idx),
+                                  oracle.all_reduce(xs, dtype, op)[0][idx.astype(np.int64)])
+
+
+def test_oracle_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter(si.rank_buffers(3, 10, "f32", "uniform"), "f32", "sum")
+    with pytest.raises(TypeError):
+        oracle.all_reduce([np.zeros(4, np.float64)], "f32", "sum")
+
+
+# ------------------------------------------------------------------ reshard
+
+def global_iota(shape):
+    return np.arange(int(np.prod(shape)), dtype=np.int32).reshape(shape)
+
+
+def local_blocks(G, layout):
+    """Expected per-rank buffers from numpy splitting of the global tensor:
+    rank l of the mesh (row-major coordinates) takes, for every Shard(d) axis
+    k, the c_k-th of dims[k] equal np.split pieces along d."""
+    dims, _start, pl = layout
+    out = []
+    for c in itertools.product(*[range(m) for m in dims]):
+        blk = G
+        for k, p in enumerate(pl):
+            if p != "R":
+                blk = np.split(blk, dims[k], axis=p[1])[c[k]]
+        out.append(np.ascontiguousarray(blk).ravel())
+    return out
+
+
+@pytest.mark.parametrize("name", ["example_a.txt", "example_b.txt"])
+def test_reshard_worked_examples(name):
+    ex = load_example(name)
+    shape = ex["shape"]
+    G = global_iota(shape)
+    src_dims, src_start, _ = ex["src"]
+    dst_dims, dst_start, _ = ex["dst"]
+    # the page's source holdings
+    src_bufs = []
+    for l in range(int(np.prod(src_dims))):
+        (r0, r1), (c0, c1) = ex["hold"]["src"][src_start + l]
+        src_bufs.append(np.ascontiguousarray(G[r0:r1, c0:c1]).ravel())
+    dst = oracle.reshard(shape, ex["src"], ex["dst"], src_bufs, fill=-1)
+    assert len(dst) == int(np.prod(dst_dims))
+    for l, buf in enumerate(dst):
+        (r0, r1), (c0, c1) = ex["hold"]["dst"][dst_start + l]
+        np.testing.assert_array_equal(buf, G[r0:r1, c0:c1].ravel())
+
+
+def test_example_a_source_holdings_follow_from_layout():
+    ex = load_example("example_a.txt")
+    G = global_iota(ex["shape"])
+    blocks = local_blocks(G, ex["src"])
+    for l, blk in enumerate(blocks):
+        (r0, r1), (c0, c1) = ex["hold"]["src"][l]
+        np.testing.assert_array_equal(blk, G[r0:r1, c0:c1].ravel())
+
+
+def test_example_a_rejects_column_major_reading():
+    """Numbering the destination mesh column-major would give ranks 4/5 rows
+    [0:2]; the page says ranks 4/6, which is what the oracle produces."""
+    ex = load_example("example_a.txt")
+    G = global_iota(ex["shape"])
+    src_bufs = local_blocks(G, ex["src"])
+    dst = oracle.reshard(ex["shape"], ex["src"], ex["dst"], src_bufs)
+    assert not np.array_equal(dst[1], G[0:2].ravel())  # rank 5 is not rows 0:2
+    np.testing.assert_array_equal(dst[2], G[0:2].ravel())  # rank 6 is
+
+
+def _tiny_layouts(ndim, shape):
+    meshes = [[1], [2], [3], [4], [2, 2], [1, 3], [3, 1], [2, 3]]
+    for dims in meshes:
+        choices = [["R"] + [("S", d) for d in range(ndim)] for _ in dims]
+        for pl in itertools.product(*choices):
+            sharded = [p for p in pl if p != "R"]
+            if len(sharded) > 1:
+                continue
+            ok = all(p == "R" or shape[p[1]] % dims[k] == 0 for k, p in enumerate(pl))
+            if ok:
+                yield dims, list(pl)
+
+
+@pytest.mark.parametrize("shape", [(6,), (4, 6), (2, 3, 4)])
+def test_reshard_all_tiny_layouts_against_numpy_split(shape):
+    G = global_iota(shape)
+    layouts = list(_tiny_layouts(len(shape), shape))
+    rng = np.random.default_rng(len(shape))
+    pairs = [(a, b) for a in layouts for b in layouts]
+    sel = rng.choice(len(pairs), size=min(300, len(pairs)), replace=False)
+    for i in sel:
+        (sd, spl), (dd, dpl) = pairs[i]
+        src = (sd, 0, spl)
+        dst = (dd, int(np.prod(sd)) + 1, dpl)
+        src_bufs = local_blocks(G, src)
+        got = oracle.reshard(shape, src, dst, src_bufs, fill=-1)
+        want = local_blocks(G, dst)
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(g, w)
+        # point queries agree with the brute force
+        for l, g in enumerate(got):
+            idx = np.arange(g.size, dtype=np.uint64)
+            np.testing.assert_array_equal(oracle.reshard_at(shape, src, dst, src_bufs, l, idx), g)
+
+
+def test_reshard_shard_to_replicate_is_all_gather():
+    P = 4
+    xs = si.rank_buffers(P, 50, "bf16", "w002", seed=3)
+    dst = oracle.reshard((P * 50,), ([P], 0, [("S", 0)]), ([3], P, ["R"]), xs)
+    for y in dst:
+        np.testing.assert_array_equal(y, np.concatenate(xs))
+
+
+def test_reshard_replicate_to_shard_is_slicing():
+    t = si.tensor((8, 5), "bf16", "w002", seed=8)
+    dst = oracle.reshard((8, 5), ([2], 0, ["R"]), ([4], 2, [("S", 0)]), [t.ravel(), t.ravel()])
+    for y, w in zip(dst, np.split(t, 4, axis=0)):
+        np.testing.assert_array_equal(y, w.ravel())
+
+
+def test_reshard_identical_layout_is_identity():
+    xs = si.rank_buffers(4, 24, "f32", "normal", seed=6)
+    dst = oracle.reshard((4, 24), ([4], 0, [("S", 0)]), ([4], 4, [("S", 0)]), xs)
+    for y, x in zip(dst, xs):
+        np.testing.assert_array_equal(y, x)
+
+
+def test_reshard_detects_disagreeing_source_replicas():
+    a = np.arange(8, dtype=np.int32)
+    b = a.copy()
+    b[3] += 1
+    with pytest.raises(ValueError):
+        oracle.reshard((8,), ([2], 0, ["R"]), ([1], 2, ["R"]), [a, b])
+
+
+@pytest.mark.parametrize("bad", [
+    dict(src=([2], 0, [("S", 0)]), dst=([2], 1, ["R"])),      # overlapping meshes
+    dict(src=([3], 0, [("S", 0)]), dst=([1], 3, ["R"])),      # 3 does not divide 8
+    dict(src=([2], 0, [("S", 5)]), dst=([1], 2, ["R"])),      # no such tensor dim
+])
+def test_reshard_rejects_invalid_layouts(bad):
+    bufs = [np.zeros(8, np.int32)] * 3
+    with pytest.raises(ValueError):
+        oracle.reshard((8,), bad["src"], bad["dst"], bufs)
+
+
+def test_torch_available_for_library_checks():
+    assert torch.tensor([1.0], dtype=torch.bfloat16).item() == 1.0
