@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark: achieved HBM GB/s of all-reduce over P=8 rank buffers of 256 MiB bf16.
+
+One step = one ccl_all_reduce call (sum, fold in fp32 in rank order, bf16 in
+and out) over 8 rank buffers of 134,217,728 bf16 each, resident in HBM before
+the timed region starts; it reads 2 GiB and writes 2 GiB.  W warmup steps run
+untimed, then K steps are timed with HIP events on the stream the kernels are
+launched on, bracketed by device synchronizations.  Rank 0 prints one JSON
+line.
+
+Besides the headline value the line carries:
+  roofline      achieved HBM GB/s of the all-reduce kernel against MI355X's
+                8 TB/s, and the HBM traffic rocprofv3 counted for it (from the
+                committed counter summary, only while the kernel source still
+                matches the one the counters were taken on);
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
+                (single thread);
+  rows          the other data-plane workloads (reduce-scatter bf16 and int32,
+                all-gather, the two weight reshards), each timed the same way.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (and % of roofline) for all_reduce P=8, 256 MB bf16"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "all_reduce_p8_256MiB_bf16_traffic.txt")
+KERNEL_SOURCES = ["ccl_collectives.hip", "ccl_device.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "collective_communication_plane_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(bytes_per_launch_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    vals = {}
+    with open(TRAFFIC_SUMMARY) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(launch, steps: int, warmup: int, stream):
+    import torch
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        launch()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps  # ms per launch
+
+
+def up(a, dev):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to(dev)
+
+
+def cpu_baseline(seconds: float = 10.0):
+    """The oracle on a bounded sample: 8 ranks x 2^22 bf16 (8 MiB each)."""
+    import numpy as np
+
+    import oracle
+    import synth_inputs as si
+
+    P, n = 8, 1 << 22
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.all_reduce(xs, "bf16", "sum")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = reps * 2 * P * n * 2 / el / 1e9
+    del np
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"all_reduce sum over 8 ranks x 4,194,304 bf16 (first 8 MiB of the "
+                      f"workload's shape, same distribution), {reps} repetitions in {el:.1f} s, "
+                      f"one thread"}
+
+
+def rows(dev, stream, steps: int, warmup: int):
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    out = {}
+
+    def record(name, nbytes, ms, desc):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"workload": desc, "hbm_bytes": nbytes, "ms": round(ms, 5),
+                     "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+    P, N = 8, 67_108_864
+    M = N // P
+    for dt, dist, code in [("bf16", "normal", ccl.CCL_BFLOAT16), ("i32", "int20", ccl.CCL_INT32)]:
+        xs = si.rank_buffers(P, N, dt, dist, seed=0)
+        dx = [up(x, dev) for x in xs]
+        del xs
+        esz = dx[0].numel() // N
+        dy = [torch.empty(M * esz, dtype=torch.uint8, device=dev) for _ in range(P)]
+        ms = timed(lambda: ccl.check(ccl.ccl_reduce_scatter(dx, dy, P, M, code, ccl.CCL_SUM, stream)),
+                   steps, warmup, stream)
+        record(f"reduce_scatter_{dt}", P * N * esz + P * M * esz, ms,
+               f"reduce_scatter sum, P=8 x 67,108,864 {dt}")
+        del dx, dy
+    torch.cuda.empty_cache()
+
+    M = 16_777_216
+    xs = si.rank_buffers(P, M, "bf16", "normal", seed=0)
+    dx = [up(x, dev) for x in xs]
+    del xs
+    dy = [torch.empty(P * M * 2, dtype=torch.uint8, device=dev) for _ in range(P)]
+    ms = timed(lambda: ccl.check(ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, stream)),
+               steps, warmup, stream)
+    record("all_gather_bf16", P * M * 2 + P * P * M * 2, ms, "all_gather, P=8 x 16,777,216 bf16")
+    del dx, dy
+    torch.cuda.empty_cache()
+
+    for name, shape, src, dst, nsrc, ndst, rho in [
+        ("reshard_weight", (8192, 28672), ([1, 4], 0, ["R", ("S", 0)]),
+         ([2, 2], 4, ["R", ("S", 0)]), 4, 4, 2),
+        ("reshard_moe", (64, 2048, 1408), ([8], 0, [("S", 0)]), ([4], 8, [("S", 1)]), 8, 4, 1),
+    ]:
+        G = si.tensor(shape, "bf16", "w002", seed=0)
+        # source mesh rank l holds its row-major block of the global tensor
+        if name == "reshard_weight":
+            blocks = np.split(G, 4, axis=0)
+        else:
+            blocks = np.split(G, 8, axis=0)
+        dsrc = [up(np.ascontiguousarray(b), dev) for b in blocks]
+        del G, blocks
+        tensor_bytes = sum(t.numel() for t in dsrc)
+        dbytes = tensor_bytes * rho // ndst
+        ddst = [torch.empty(dbytes, dtype=torch.uint8, device=dev) for _ in range(ndst)]
+        st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
+                                        ccl.make_mesh(src[0], src[1]), ccl.make_placements(src[2]),
+                                        ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))
+        ccl.check(st, "reshard_plan")
+        ms = timed(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream)), steps,
+                   warmup, stream)
+        ccl.check(ccl.ccl_plan_destroy(plan))
+        record(name, tensor_bytes * (1 + rho), ms,
+               f"reshard {list(shape)} bf16 {src} -> {dst}")
+        del dsrc, ddst
+        torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true")
+    ap.add_argument("--row-steps", type=int, default=50)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the data plane runs over P simulated rank buffers in "
+              "one GPU's HBM, so there is no multi-GPU run (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    ccl._load()  # fails loudly if libccl.so is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    P, n = 8, 134_217_728
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
+    dx = [up(x, dev) for x in xs]
+    dy = [torch.empty_like(t) for t in dx]
+    bytes_per_step = 2 * P * n * 2
+
+    def step():
+        ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream),
+                  "all_reduce")
+
+    torch.cuda.synchronize()
+    ms = timed(step, args.steps, args.warmup, stream)
+    value = bytes_per_step / (ms * 1e-3) / 1e9
+
+    # spot-check the timed outputs against the oracle
+    import oracle
+
+    idx = si.sample_indices(n, 4096, seed=5)
+    it = torch.from_numpy(idx.astype(np.int64)).to(dev)
+    got = dy[P - 1].view(torch.int16)[it].cpu().numpy().view(np.uint16)
+    want = oracle.fold_at(xs, "bf16", "sum", idx)
+    parity = bool(np.array_equal(got, want))
+    del xs
+
+    traffic = read_traffic(bytes_per_step)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "all_reduce sum, P=8 rank buffers x 134,217,728 bf16 (256 MiB) each, "
+                        "uniform[-1,1) seed 0, fp32 fold in rank order, bf16 out",
+            "P": P, "count": n, "storage_dtype": "bf16", "accumulate": "f32",
+            "hbm_bytes_per_step": bytes_per_step, "launch": "library defaults",
+            "parity_spot_check": parity,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+        },
+    }
+    del dx, dy
+    torch.cuda.empty_cache()
+    if not args.no_rows:
+        line["rows"] = rows(dev, stream, args.row_steps, 5)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+    return 0 if parity else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,219 @@
+// C ABI entry points of libccl: argument checks (fail-stop: nothing is
+// enqueued unless every check passes), launch-config resolution, and dispatch
+// to the kernels in ccl_collectives.hip / ccl_reshard.hip.
+#include <cstdint>
+#include <cstring>
+
+#include "ccl_internal.h"
+
+namespace {
+
+using ccl::dtype_size;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool mul_overflows(uint64_t a, uint64_t b) { return b != 0 && a > UINT64_MAX / b; }
+
+ccl_status_t check_common(const void *const *send, void *const *recv, int nranks, int dtype) {
+  if (nranks < 1 || nranks > CCL_MAX_RANKS) return CCL_ERR_INVALID_ARG;
+  if (dtype_size(dtype) == 0) return CCL_ERR_INVALID_ARG;
+  if (!send || !recv) return CCL_ERR_INVALID_ARG;
+  const uintptr_t align = (uintptr_t)dtype_size(dtype);
+  for (int r = 0; r < nranks; ++r) {
+    if (!send[r] || !recv[r]) return CCL_ERR_INVALID_ARG;
+    if (((uintptr_t)send[r] % align) || ((uintptr_t)recv[r] % align)) return CCL_ERR_INVALID_ARG;
+  }
+  return CCL_OK;
+}
+
+bool op_ok(int op) { return op == CCL_SUM || op == CCL_MIN || op == CCL_MAX; }
+
+// Outputs must not overlap each other at all.
+ccl_status_t check_outputs_disjoint(void *const *recv, int P, uint64_t bytes) {
+  for (int a = 0; a < P; ++a)
+    for (int b = a + 1; b < P; ++b) {
+      Range ra{(uintptr_t)recv[a], (uintptr_t)recv[a] + bytes};
+      Range rb{(uintptr_t)recv[b], (uintptr_t)recv[b] + bytes};
+      if (overlap(ra, rb)) return CCL_ERR_ALIASING;
+    }
+  return CCL_OK;
+}
+
+}  // namespace
+
+namespace ccl {
+
+int device_cu_count(int dev) {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  if (dev < 0 || dev >= 64) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out) {
+  Launch l{kDefaultChunkBytes, 0, 1, 2, true, true};
+  if (cfg) {
+    if (cfg->chunk_bytes) {
+      if (cfg->chunk_bytes % kVecBytes || cfg->chunk_bytes < 1024 ||
+          cfg->chunk_bytes > (uint64_t(1) << 32))
+        return CCL_ERR_INVALID_ARG;
+      l.chunk_bytes = cfg->chunk_bytes;
+    }
+    if (cfg->workgroups < 0 || cfg->workgroups > (1 << 24)) return CCL_ERR_INVALID_ARG;
+    l.workgroups = cfg->workgroups;
+    if (cfg->stages < 0 || cfg->stages > 4) return CCL_ERR_INVALID_ARG;
+    if (cfg->stages) l.stages = cfg->stages;
+    if (cfg->unroll < 0 || cfg->unroll > 2) return CCL_ERR_INVALID_ARG;
+    if (cfg->unroll) l.unroll = cfg->unroll;
+    if (cfg->nontemporal < 0 || cfg->nontemporal > 4) return CCL_ERR_INVALID_ARG;
+    if (cfg->nontemporal == 4) {
+      l.nt_load = l.nt_store = false;
+    } else if (cfg->nontemporal) {
+      l.nt_load = cfg->nontemporal & 1;
+      l.nt_store = (cfg->nontemporal >> 1) & 1;
+    }
+    if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) return CCL_ERR_INVALID_ARG;
+  }
+  *out = l;
+  return CCL_OK;
+}
+
+}  // namespace ccl
+
+extern "C" {
+
+const char *ccl_get_error_string(ccl_status_t s) {
+  switch (s) {
+    case CCL_OK: return "success";
+    case CCL_ERR_INVALID_ARG: return "invalid argument";
+    case CCL_ERR_UNSUPPORTED: return "unsupported request";
+    case CCL_ERR_ALIASING: return "illegal buffer overlap";
+    case CCL_ERR_LAYOUT: return "invalid reshard layout";
+    case CCL_ERR_HIP: return "HIP runtime error";
+    case CCL_ERR_NOMEM: return "out of memory";
+  }
+  return "unknown status";
+}
+
+int ccl_version(void) { return 100; }
+
+ccl_status_t ccl_all_reduce(const void *const *send, void *const *recv, int nranks, size_t count,
+                            int dtype, int op, void *stream, const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
+    return CCL_ERR_INVALID_ARG;
+  if (count == 0) return CCL_OK;
+  if ((st = check_common(send, recv, nranks, dtype))) return st;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(count, sz)) return CCL_ERR_INVALID_ARG;
+  const uint64_t bytes = count * sz;
+  if ((st = check_outputs_disjoint(recv, nranks, bytes))) return st;
+  // An output may coincide exactly with an input: element i is read and then
+  // written by the same lane.  Any other overlap would race.
+  for (int q = 0; q < nranks; ++q)
+    for (int r = 0; r < nranks; ++r) {
+      Range y{(uintptr_t)recv[q], (uintptr_t)recv[q] + bytes};
+      Range x{(uintptr_t)send[r], (uintptr_t)send[r] + bytes};
+      if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
+    }
+  ccl::CollDesc d{ccl::KIND_AR, nranks, dtype, op, count, send, recv};
+  return ccl::launch_collective(d, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int nranks,
+                                size_t recvcount, int dtype, int op, void *stream,
+                                const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
+    return CCL_ERR_INVALID_ARG;
+  if (recvcount == 0) return CCL_OK;
+  if ((st = check_common(send, recv, nranks, dtype))) return st;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(recvcount, sz) || mul_overflows(recvcount * sz, (uint64_t)nranks))
+    return CCL_ERR_INVALID_ARG;
+  const uint64_t out_bytes = recvcount * sz, in_bytes = out_bytes * nranks;
+  if ((st = check_outputs_disjoint(recv, nranks, out_bytes))) return st;
+  // recv[s] may sit exactly on shard s of an input (the NCCL in-place form).
+  for (int s = 0; s < nranks; ++s)
+    for (int r = 0; r < nranks; ++r) {
+      Range y{(uintptr_t)recv[s], (uintptr_t)recv[s] + out_bytes};
+      Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
+      if (overlap(x, y) && y.lo != x.lo + (uint64_t)s * out_bytes) return CCL_ERR_ALIASING;
+    }
+  ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, recvcount, send, recv};
+  return ccl::launch_collective(d, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nranks,
+                            size_t sendcount, int dtype, void *stream,
+                            const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0) return CCL_ERR_INVALID_ARG;
+  if (sendcount == 0) return CCL_OK;
+  if ((st = check_common(send, recv, nranks, dtype))) return st;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(sendcount, sz) || mul_overflows(sendcount * sz, (uint64_t)nranks))
+    return CCL_ERR_INVALID_ARG;
+  const uint64_t in_bytes = sendcount * sz, out_bytes = in_bytes * nranks;
+  if ((st = check_outputs_disjoint(recv, nranks, out_bytes))) return st;
+  // send[r] may sit exactly on slot r of an output (the NCCL in-place form).
+  for (int q = 0; q < nranks; ++q)
+    for (int r = 0; r < nranks; ++r) {
+      Range y{(uintptr_t)recv[q], (uintptr_t)recv[q] + out_bytes};
+      Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
+      if (overlap(x, y) && x.lo != y.lo + (uint64_t)r * in_bytes) return CCL_ERR_ALIASING;
+    }
+  ccl::CollDesc d{ccl::KIND_AG, nranks, dtype, CCL_SUM, sendcount, send, recv};
+  return ccl::launch_collective(d, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_bufs,
+                              void *const *dst_bufs, void *stream,
+                              const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  if (st) return st;
+  if (!plan || !src_bufs || !dst_bufs) return CCL_ERR_INVALID_ARG;
+  ccl_plan *p = const_cast<ccl_plan *>(plan);
+  const uintptr_t align = (uintptr_t)p->elem_size;
+  for (int i = 0; i < p->n_src; ++i)
+    if (p->src_local_bytes[i] && (!src_bufs[i] || (uintptr_t)src_bufs[i] % align))
+      return CCL_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_dst; ++i)
+    if (p->dst_local_bytes[i] && (!dst_bufs[i] || (uintptr_t)dst_bufs[i] % align))
+      return CCL_ERR_INVALID_ARG;
+  for (int a = 0; a < p->n_dst; ++a) {
+    Range ra{(uintptr_t)dst_bufs[a], (uintptr_t)dst_bufs[a] + p->dst_local_bytes[a]};
+    if (ra.lo == ra.hi) continue;
+    for (int b = a + 1; b < p->n_dst; ++b) {
+      Range rb{(uintptr_t)dst_bufs[b], (uintptr_t)dst_bufs[b] + p->dst_local_bytes[b]};
+      if (rb.lo != rb.hi && overlap(ra, rb)) return CCL_ERR_ALIASING;
+    }
+    for (int s = 0; s < p->n_src; ++s) {
+      Range rs{(uintptr_t)src_bufs[s], (uintptr_t)src_bufs[s] + p->src_local_bytes[s]};
+      if (rs.lo != rs.hi && overlap(ra, rs)) return CCL_ERR_ALIASING;
+    }
+  }
+  if (p->intervals.empty()) return CCL_OK;
+  if (l.stages != 1) return CCL_ERR_UNSUPPORTED;  // the copy has no LDS pipeline
+  return ccl::reshard_launch(p, src_bufs, dst_bufs, l, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device helpers for the gfx950 kernels: 16-byte vector memory access with
+// optional nontemporal hints, bf16 widening / round-to-nearest-even
+// narrowing, and the element-wise fold in rank order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ccl.h"
+
+namespace ccl {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld_plain(const char *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ u32x4 ld_nt(const char *p) {
+  return __builtin_nontemporal_load((const u32x4 *)p);
+}
+__device__ __forceinline__ void st_plain(char *p, u32x4 v) { *(u32x4 *)p = v; }
+__device__ __forceinline__ void st_nt(char *p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4 *)p); }
+
+// bf16 -> fp32 is exact: the bf16 pattern is the upper half of the fp32 one.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits (in the low 16 bits), round to nearest, ties to even;
+// NaN becomes the canonical quiet NaN 0x7fc0.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
+}
+
+// One fold step.  min/max are compare-and-select so a tie (including +0 vs
+// -0) keeps the accumulated (earlier-rank) value.
+template <int OP>
+__device__ __forceinline__ float fold_f32(float acc, float v) {
+  if constexpr (OP == CCL_SUM) return acc + v;
+  else if constexpr (OP == CCL_MIN) return (v < acc) ? v : acc;
+  else return (v > acc) ? v : acc;
+}
+
+template <int OP>
+__device__ __forceinline__ int32_t fold_i32(int32_t acc, int32_t v) {
+  if constexpr (OP == CCL_SUM) return (int32_t)((uint32_t)acc + (uint32_t)v);
+  else if constexpr (OP == CCL_MIN) return (v < acc) ? v : acc;
+  else return (v > acc) ? v : acc;
+}
+
+// Fold the first n (runtime, <= NI) vectors of x element-wise in rank order.
+template <int DT, int OP, int NI>
+__device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[NI], int n) {
+  u32x4 y;
+  if constexpr (DT == CCL_BFLOAT16) {
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[2 * k] = bf16_lo(x[0][k]);
+      a[2 * k + 1] = bf16_hi(x[0][k]);
+    }
+#pragma unroll
+    for (int r = 1; r < NI; ++r) {
+      if (r < n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[2 * k] = fold_f32<OP>(a[2 * k], bf16_lo(x[r][k]));
+          a[2 * k + 1] = fold_f32<OP>(a[2 * k + 1], bf16_hi(x[r][k]));
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = bf16_rne(a[2 * k]) | (bf16_rne(a[2 * k + 1]) << 16);
+  } else if constexpr (DT == CCL_FLOAT32) {
+    float a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = __uint_as_float(x[0][k]);
+#pragma unroll
+    for (int r = 1; r < NI; ++r)
+      if (r < n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = fold_f32<OP>(a[k], __uint_as_float(x[r][k]));
+      }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = __float_as_uint(a[k]);
+  } else {
+    int32_t a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = (int32_t)x[0][k];
+#pragma unroll
+    for (int r = 1; r < NI; ++r)
+      if (r < n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a[k] = fold_i32<OP>(a[k], (int32_t)x[r][k]);
+      }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = (uint32_t)a[k];
+  }
+  return y;
+}
+
+}  // namespace ccl

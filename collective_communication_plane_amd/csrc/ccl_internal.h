@@ -1,0 +1,96 @@
+// Internal declarations shared by the libccl translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "ccl.h"
+
+namespace ccl {
+
+constexpr int kVecBytes = 16;          // one dwordx4 per lane
+constexpr int kThreads = 256;          // register-direct workgroup: 4 wave64s
+constexpr int kLdsTileBytes = 4096;    // LDS pipeline: per-rank bytes per stage
+constexpr uint64_t kDefaultChunkBytes = 64 * 1024;
+
+inline int dtype_size(int dt) {
+  switch (dt) {
+    case CCL_FLOAT32: return 4;
+    case CCL_BFLOAT16: return 2;
+    case CCL_INT32: return 4;
+    default: return 0;
+  }
+}
+
+enum Kind { KIND_AR = 0, KIND_RS = 1, KIND_AG = 2 };
+
+// A fully resolved launch configuration.
+struct Launch {
+  uint64_t chunk_bytes;
+  int workgroups;  // 0 = derive from the chunk count
+  int stages;      // 1 = register-direct, 2..4 = LDS pipeline
+  int unroll;      // 1 or 2
+  bool nt_load;
+  bool nt_store;
+};
+
+// Collective launch description, all checks already passed.
+struct CollDesc {
+  Kind kind;
+  int P;
+  int dtype;
+  int op;
+  uint64_t seg_elems;  // AR: count, RS: recvcount, AG: sendcount
+  const void *const *send;
+  void *const *recv;
+};
+
+// Compute units of a device (cached after the first query); <= 0 on error.
+int device_cu_count(int dev);
+
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out);
+ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t stream);
+
+// ------------------------------------------------------------------ reshard
+
+struct PlanInterval {
+  int32_t src_local;   // index of the source rank inside the source mesh
+  int32_t dst_shard;   // destination shard
+  int32_t leader;      // global rank of the leading replica
+  uint64_t src_off;    // bytes
+  uint64_t dst_off;    // bytes
+  uint64_t len;        // bytes
+};
+
+struct DevicePlanCache {
+  int device = -1;
+  void *table = nullptr;  // device copy of the interval + replica tables
+  uint64_t chunk_bytes = 0;
+  uint64_t total_chunks = 0;
+};
+
+}  // namespace ccl
+
+struct ccl_plan {
+  int32_t elem_size;
+  int32_t src_start, dst_start;
+  int32_t n_src, n_dst;                 // ranks in each mesh
+  int32_t n_dst_shards;
+  std::vector<uint64_t> src_local_bytes;  // per source-mesh rank
+  std::vector<uint64_t> dst_local_bytes;  // per destination-mesh rank
+  std::vector<std::vector<int32_t>> replicas;  // per dst shard: local dst indices, ascending
+  std::vector<ccl::PlanInterval> intervals;
+  // Device-side state, created on first use.
+  std::mutex mu;
+  std::vector<ccl::DevicePlanCache> dev;
+};
+
+namespace ccl {
+ccl_status_t reshard_launch(ccl_plan *plan, const void *const *src, void *const *dst,
+                            const Launch &l, hipStream_t stream);
+void reshard_release(ccl_plan *plan);
+}  // namespace ccl

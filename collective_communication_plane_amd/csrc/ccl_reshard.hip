@@ -1,0 +1,197 @@
+// Reshard copy kernel for gfx950: executes a plan of byte intervals with
+// one load and rho stores per 16-byte vector.
+//
+// The "NCCL M2N vs T-CCL" digest (lqnn.cn news 207677) s1.2 and its s1.4
+// device-side sketch describe the data plane: each source contribution enters
+// a destination shard once (at a leader) and the shard's other replicas are
+// filled by local copies.  On one GPU both steps collapse into one pass: the
+// bytes of an interval are loaded once into VGPRs and stored to every replica,
+// so a shard with rho replicas costs 1 read + rho writes instead of the
+// 1 + 1 + 2(rho - 1) of a leader-then-copy scheme.
+//
+// Work decomposition: every interval is cut into chunks of chunk_bytes;
+// chunk c of the plan belongs to the interval whose first chunk index is the
+// largest one <= c (binary search over a prefix table).  Chunks are dealt to
+// workgroups round-robin.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "ccl_device.h"
+#include "ccl_internal.h"
+
+namespace ccl {
+namespace {
+
+constexpr int kReshardUnroll = 4;
+
+struct DevInterval {
+  uint64_t src_off;
+  uint64_t dst_off;
+  uint64_t len;
+  uint64_t first_chunk;
+  int32_t src_local;
+  int32_t dst_shard;
+};
+
+struct ReshardArgs {
+  const char *src[CCL_MAX_MESH_RANKS];
+  char *dst[CCL_MAX_MESH_RANKS];
+  const DevInterval *iv;
+  const int32_t *rep;  // rep[shard * rho + j] = local index of replica j
+  uint64_t total_chunks;
+  uint64_t chunk_bytes;
+  int n_iv;
+  int rho;
+  int flags;           // bit 0: nontemporal loads, bit 1: nontemporal stores
+};
+
+__device__ __forceinline__ int find_interval(const DevInterval *iv, int n, uint64_t c) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (iv[mid].first_chunk <= c) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
+    const int i = find_interval(a.iv, a.n_iv, c);
+    const DevInterval iv = a.iv[i];
+    const uint64_t off = (c - iv.first_chunk) * a.chunk_bytes;
+    const uint64_t bytes = min(a.chunk_bytes, iv.len - off);
+    const char *src = a.src[iv.src_local] + iv.src_off + off;
+    const int32_t *rep = a.rep + (uint64_t)iv.dst_shard * a.rho;
+    const uint64_t dst_base = iv.dst_off + off;
+
+    // Vector path when every address shares the source's alignment mod 16.
+    const uintptr_t mis = (uintptr_t)src % kVecBytes;
+    bool same = true;
+    for (int j = 0; j < a.rho; ++j)
+      same &= ((uintptr_t)(a.dst[rep[j]] + dst_base) % kVecBytes) == mis;
+    if (!same) {
+      for (uint64_t b = threadIdx.x; b < bytes; b += kThreads) {
+        const char v = src[b];
+        for (int j = 0; j < a.rho; ++j) a.dst[rep[j]][dst_base + b] = v;
+      }
+      continue;
+    }
+    const uint64_t head = min<uint64_t>((kVecBytes - mis) % kVecBytes, bytes);
+    const uint64_t nvec = (bytes - head) / kVecBytes;
+    const uint64_t tail0 = head + nvec * kVecBytes;
+    if (threadIdx.x < head) {
+      const char v = src[threadIdx.x];
+      for (int j = 0; j < a.rho; ++j) a.dst[rep[j]][dst_base + threadIdx.x] = v;
+    } else if (threadIdx.x - head < bytes - tail0) {
+      const uint64_t b = tail0 + (threadIdx.x - head);
+      const char v = src[b];
+      for (int j = 0; j < a.rho; ++j) a.dst[rep[j]][dst_base + b] = v;
+    }
+    const char *vs = src + head;
+    for (uint64_t v = threadIdx.x; v < nvec; v += (uint64_t)kThreads * kReshardUnroll) {
+      u32x4 x[kReshardUnroll];
+#pragma unroll
+      for (int u = 0; u < kReshardUnroll; ++u) {
+        const uint64_t vv = v + (uint64_t)u * kThreads;
+        if (vv < nvec) x[u] = ntl ? ld_nt(vs + vv * kVecBytes) : ld_plain(vs + vv * kVecBytes);
+      }
+      for (int j = 0; j < a.rho; ++j) {
+        char *d = a.dst[rep[j]] + dst_base + head;
+#pragma unroll
+        for (int u = 0; u < kReshardUnroll; ++u) {
+          const uint64_t vv = v + (uint64_t)u * kThreads;
+          if (vv < nvec) {
+            if (nts) st_nt(d + vv * kVecBytes, x[u]);
+            else st_plain(d + vv * kVecBytes, x[u]);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Build (or find) the device copy of the plan for this device and chunk size.
+ccl_status_t device_table(ccl_plan *p, int dev, uint64_t chunk_bytes, DevicePlanCache *out) {
+  std::lock_guard<std::mutex> lock(p->mu);
+  for (const auto &e : p->dev)
+    if (e.device == dev && e.chunk_bytes == chunk_bytes) {
+      *out = e;
+      return CCL_OK;
+    }
+  const size_t n = p->intervals.size();
+  const int rho = p->n_dst / p->n_dst_shards;
+  std::vector<DevInterval> host(n);
+  uint64_t chunk = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const PlanInterval &iv = p->intervals[i];
+    host[i] = DevInterval{iv.src_off, iv.dst_off, iv.len, chunk, iv.src_local, iv.dst_shard};
+    chunk += (iv.len + chunk_bytes - 1) / chunk_bytes;
+  }
+  std::vector<int32_t> rep((size_t)p->n_dst_shards * rho);
+  for (int t = 0; t < p->n_dst_shards; ++t)
+    for (int j = 0; j < rho; ++j) rep[(size_t)t * rho + j] = p->replicas[t][j];
+  const size_t iv_bytes = n * sizeof(DevInterval);
+  const size_t bytes = iv_bytes + rep.size() * sizeof(int32_t);
+  void *mem = nullptr;
+  if (hipMalloc(&mem, bytes) != hipSuccess) return CCL_ERR_NOMEM;
+  // Synchronous copies: the host staging vectors die when this returns.
+  if (hipMemcpy(mem, host.data(), iv_bytes, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy((char *)mem + iv_bytes, rep.data(), rep.size() * sizeof(int32_t),
+                hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(mem);
+    return CCL_ERR_HIP;
+  }
+  DevicePlanCache e;
+  e.device = dev;
+  e.table = mem;
+  e.chunk_bytes = chunk_bytes;
+  e.total_chunks = chunk;
+  p->dev.push_back(e);
+  *out = e;
+  return CCL_OK;
+}
+
+}  // namespace
+
+ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *dst,
+                            const Launch &l, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
+  const int cus = device_cu_count(dev);
+  if (cus <= 0) return CCL_ERR_HIP;
+  DevicePlanCache e;
+  ccl_status_t st = device_table(p, dev, l.chunk_bytes, &e);
+  if (st) return st;
+  ReshardArgs a{};
+  for (int i = 0; i < p->n_src; ++i) a.src[i] = (const char *)src[i];
+  for (int i = 0; i < p->n_dst; ++i) a.dst[i] = (char *)dst[i];
+  a.iv = (const DevInterval *)e.table;
+  a.rep = (const int32_t *)((const char *)e.table + p->intervals.size() * sizeof(DevInterval));
+  a.total_chunks = e.total_chunks;
+  a.chunk_bytes = l.chunk_bytes;
+  a.n_iv = (int)p->intervals.size();
+  a.rho = p->n_dst / p->n_dst_shards;
+  a.flags = (l.nt_load ? 1 : 0) | (l.nt_store ? 2 : 0);
+  uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
+  grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+}
+
+void reshard_release(ccl_plan *p) {
+  std::lock_guard<std::mutex> lock(p->mu);
+  for (auto &e : p->dev) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(e.device);
+    (void)hipFree(e.table);
+    (void)hipSetDevice(cur);
+  }
+  p->dev.clear();
+}
+
+}  // namespace ccl

@@ -1,0 +1,247 @@
+/*
+ * ccl.h -- C ABI of libccl: the reduce and copy data plane of a collective
+ * library, run on one GPU over P simulated rank buffers resident in its HBM.
+ *
+ * Sources (web pages this library is built from):
+ *   [digest]  "NCCL M2N vs T-CCL" digest, lqnn.cn news 207677.
+ *   [roadmap] "nccl-extensions" page, an explainer of NCCL's roadmap; its
+ *             "NCCL API overview" table (host API collectives such as
+ *             all-reduce) and its GENK section (ring all-gather,
+ *             reduce-scatter, all-reduce built from receive/reduce/send parts).
+ *
+ * Conventions shared by every call:
+ *   - Buffers are device memory (or memory the current device can address),
+ *     owned by the caller.  The library never allocates or frees them.
+ *     Pointer arrays (send[], recv[], src_bufs[], dst_bufs[]) are host arrays
+ *     read only during the call.
+ *   - Every pointer must be aligned to its element size.  16-byte aligned
+ *     buffers take the wide vector path; anything else is still correct but
+ *     runs a slower element-wise kernel.
+ *   - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *     it and the call returns without waiting.  The library creates no
+ *     streams and never synchronizes them.
+ *   - Fail-stop: every argument is checked before anything is enqueued, so a
+ *     return other than CCL_OK means no kernel was launched and no output byte
+ *     was touched.  CCL_ERR_HIP reports a failed launch; faults inside a
+ *     kernel surface at the caller's next synchronization.
+ *   - A count of 0 is a valid no-op (pointers are then not inspected).
+ *   - Reductions are computed per element as a fold in rank order 0..P-1 that
+ *     starts from rank 0's value and accumulates in fp32 (bf16 inputs are
+ *     widened exactly, the fp32 result is rounded to bf16 once, to nearest
+ *     even; int32 sums wrap).  min and max keep the earlier rank's value on a
+ *     tie.  Results therefore do not depend on the launch configuration.
+ *     [digest] s2.1 gives the op set (add, min, max); the order and
+ *     accumulator type are this library's choice, fixed so results are
+ *     reproducible.
+ */
+#ifndef CCL_H
+#define CCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CCL_OK = 0,
+    CCL_ERR_INVALID_ARG = 1, /* NULL pointer, bad count/P/dtype/op, misaligned pointer */
+    CCL_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    CCL_ERR_ALIASING = 3,    /* buffers overlap in a way the op cannot run in place */
+    CCL_ERR_LAYOUT = 4,      /* reshard layout violates a constraint */
+    CCL_ERR_HIP = 5,         /* a HIP runtime call failed */
+    CCL_ERR_NOMEM = 6        /* host or device allocation for library state failed */
+} ccl_status_t;
+
+typedef enum { CCL_FLOAT32 = 0, CCL_BFLOAT16 = 1, CCL_INT32 = 2 } ccl_dtype_t;
+
+/* [digest] s2.1: the reduction operations the bulk-reduce primitive offers. */
+typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
+
+#define CCL_MAX_RANKS 16        /* P limit of the collectives */
+#define CCL_MAX_MESH_DIMS 4     /* axes of a reshard mesh */
+#define CCL_MAX_TENSOR_DIMS 8   /* dims of a resharded tensor */
+#define CCL_MAX_MESH_RANKS 64   /* ranks of one reshard mesh */
+
+/*
+ * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
+ * configuration is tuned by a sweep).  Pass NULL for the built-in defaults.
+ * A zero field means "default"; out-of-range values give CCL_ERR_INVALID_ARG.
+ * None of these fields changes any result.
+ *
+ *   chunk_bytes  contiguous bytes of each rank buffer one workgroup owns per
+ *                scheduling step (its share of a shard); a multiple of 16,
+ *                at least 1024 (for the LDS pipeline, a multiple of the
+ *                pipeline's tile, 4096).
+ *   workgroups   grid size; chunks are dealt to workgroups round-robin.
+ *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS
+ *                pipeline: producer waves stream tiles into a ring of
+ *                `stages` LDS buffers with asynchronous global->LDS loads,
+ *                consumer waves fold and store them.
+ *   unroll       register-direct only: 16-byte vectors each lane keeps in
+ *                flight per rank (1 or 2).
+ *   nontemporal  bit 0: nontemporal loads, bit 1: nontemporal stores;
+ *                0 = default (both), 4 = neither.
+ */
+typedef struct {
+    uint64_t chunk_bytes;
+    int32_t workgroups;
+    int32_t stages;
+    int32_t unroll;
+    int32_t nontemporal;
+} ccl_launch_config_t;
+
+/*
+ * All-reduce ([roadmap] API overview and GENK; [digest] s2.5, where an
+ * all-reduce is a shard-in followed by a shard-out).  For every element index
+ * i < count and every rank q: recv[q][i] = fold over r of send[r][i].
+ * The two phases are fused: each shard's reduced value stays in registers and
+ * is stored to all P outputs, so it never makes an extra trip through HBM.
+ *
+ *   send   P pointers, each to `count` elements of dtype.
+ *   recv   P pointers, each to `count` elements of dtype.
+ *   In place: recv[q] == send[q] is allowed (as is any recv[q] == send[r]);
+ *   any other overlap between buffers, or of two recv buffers, gives
+ *   CCL_ERR_ALIASING.
+ */
+ccl_status_t ccl_all_reduce(const void *const *send, void *const *recv, int nranks, size_t count,
+                            int dtype, int op, void *stream, const ccl_launch_config_t *cfg);
+
+/*
+ * Reduce-scatter, the shard-in ([digest] s2.2: the owner of a shard loads
+ * every peer's contribution and reduces it locally, with no cross-device
+ * atomics; s2.3: the logical tensor is cut into P shards, shard s owned by
+ * rank s).  For s < P, j < recvcount:
+ *   recv[s][j] = fold over r of send[r][s*recvcount + j].
+ *
+ *   send   P pointers, each to P*recvcount elements.
+ *   recv   P pointers, each to recvcount elements.
+ *   In place: recv[s] == send[s] + s*recvcount elements is allowed (the
+ *   NCCL convention); other overlaps give CCL_ERR_ALIASING.
+ */
+ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int nranks,
+                                size_t recvcount, int dtype, int op, void *stream,
+                                const ccl_launch_config_t *cfg);
+
+/*
+ * All-gather, the shard-out ([digest] s2.2: the owner loads its final shard
+ * once and stores that one copy to every peer).  For q, r < P, j < sendcount:
+ *   recv[q][r*sendcount + j] = send[r][j].
+ *
+ *   send   P pointers, each to sendcount elements.
+ *   recv   P pointers, each to P*sendcount elements.
+ *   In place: send[r] == recv[r] + r*sendcount elements is allowed;
+ *   other overlaps give CCL_ERR_ALIASING.  dtype only sets the element size.
+ */
+ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nranks,
+                            size_t sendcount, int dtype, void *stream,
+                            const ccl_launch_config_t *cfg);
+
+/* ------------------------------------------------------------------ reshard
+ * Layout-aware M-to-N reshard ([digest] s1.2 and s1.3): a tensor laid out
+ * over a source mesh with one placement per mesh axis is moved to another
+ * layout over a disjoint destination mesh.  Only the byte intervals each
+ * destination rank needs are moved, found by intersecting index boxes; a
+ * destination shard held by several replicas is read once and stored to all
+ * of them (the single-GPU form of "one leader per domain, then local copies").
+ */
+
+typedef enum { CCL_REPLICATE = 0, CCL_SHARD = 1 } ccl_placement_kind_t;
+
+/* Replicate(), or Shard(dim): dim is split into mesh-axis-size equal blocks. */
+typedef struct {
+    int32_t kind;
+    int32_t dim;
+} ccl_placement_t;
+
+/* A mesh: ndims axes of the given sizes over the contiguous global ranks
+ * start_rank .. start_rank + prod(dims) - 1, numbered row-major (last axis
+ * fastest) -- the reading [digest] s1.4 Example A pins. */
+typedef struct {
+    int32_t ndims;
+    int32_t start_rank;
+    int64_t dims[CCL_MAX_MESH_DIMS];
+} ccl_mesh_t;
+
+/* The global tensor: row-major and contiguous on every rank. */
+typedef struct {
+    int32_t ndim;
+    int32_t dtype; /* ccl_dtype_t; only its size matters to a copy */
+    int64_t shape[CCL_MAX_TENSOR_DIMS];
+} ccl_tensor_desc_t;
+
+/* One planned byte interval (inspection only). */
+typedef struct {
+    int32_t src_rank;      /* global rank the bytes are read from (lowest source replica) */
+    int32_t dst_shard;     /* destination shard index; its replicas all receive the bytes */
+    int32_t leader;        /* global rank of the replica that leads this interval */
+    int32_t num_replicas;  /* replicas of dst_shard */
+    uint64_t src_offset;   /* byte offset in the source rank's local buffer */
+    uint64_t dst_offset;   /* byte offset in every replica's local buffer */
+    uint64_t length;       /* bytes */
+} ccl_interval_t;
+
+typedef struct ccl_plan ccl_plan_t;
+
+/*
+ * Plan a reshard on the host ([digest] s1.2: the transfer plan is derived from
+ * the (mesh, placement) descriptors; intersecting intervals gives a
+ * deterministic global plan with no over-delivery; leaders are picked so that
+ * their loads differ by at most one).  Pure host code: no HIP call.
+ *
+ * Constraints ([digest] s1.3), each CCL_ERR_LAYOUT when broken: the meshes
+ * are disjoint rank ranges; at most one mesh axis per layout is Shard; the
+ * sharded tensor dim is divisible by that axis's size; every mesh has at most
+ * CCL_MAX_MESH_RANKS ranks.  Malformed descriptors give CCL_ERR_INVALID_ARG.
+ *
+ * Intervals are maximal row-major runs, sorted by (dst_shard, dst_offset);
+ * together they tile every destination shard exactly once.  *plan_out is
+ * owned by the caller and released with ccl_plan_destroy.
+ */
+ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t *src_mesh,
+                              const ccl_placement_t *src_placements, const ccl_mesh_t *dst_mesh,
+                              const ccl_placement_t *dst_placements, ccl_plan_t **plan_out);
+
+/*
+ * Execute a plan ([digest] s1.4, device data plane: each contribution enters
+ * the destination shard once and is fanned out to the other replicas; here
+ * one pass loads it once and stores it to every replica).
+ *
+ *   src_bufs   one pointer per source-mesh rank, in mesh order (rank
+ *              start_rank + l at index l), each to that rank's local block.
+ *   dst_bufs   one pointer per destination-mesh rank, likewise.
+ *   Any overlap of two destination buffers, or of a source and a
+ *   destination buffer, gives CCL_ERR_ALIASING.
+ * The first call on a device copies the plan's interval table to device
+ * memory (stream-ordered, then cached in the plan until ccl_plan_destroy).
+ */
+ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_bufs,
+                              void *const *dst_bufs, void *stream,
+                              const ccl_launch_config_t *cfg);
+
+/* Release a plan and its device table.  Work that uses it must be complete. */
+ccl_status_t ccl_plan_destroy(ccl_plan_t *plan);
+
+/* Inspection: interval count, one interval, local buffer bytes of a mesh rank
+ * (side 0 = source, 1 = destination; index = position in that mesh), the
+ * replicas of a destination shard (global ranks, ascending), and the number
+ * of distinct destination shards. */
+ccl_status_t ccl_plan_num_intervals(const ccl_plan_t *plan, uint64_t *count);
+ccl_status_t ccl_plan_get_interval(const ccl_plan_t *plan, uint64_t i, ccl_interval_t *out);
+ccl_status_t ccl_plan_local_bytes(const ccl_plan_t *plan, int side, int index, uint64_t *bytes);
+ccl_status_t ccl_plan_num_dst_shards(const ccl_plan_t *plan, int32_t *count);
+ccl_status_t ccl_plan_shard_replicas(const ccl_plan_t *plan, int32_t dst_shard, int32_t *ranks,
+                                     int32_t capacity, int32_t *count);
+
+/* A static, human-readable name for a status code. */
+const char *ccl_get_error_string(ccl_status_t status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int ccl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CCL_H */

@@ -80,3 +80,34 @@ def sample_indices(n: int, k: int, seed: int = 1) -> np.ndarray:
     idx = rng.integers(0, n, size=min(k, n), dtype=np.int64)
     idx = np.unique(np.concatenate([idx, [0, n - 1]]))
     return idx.astype(np.uint64)
+
+
+def device_rank_buffers(P: int, n: int, dtype: str, dist: str, seed: int, device):
+    """P device tensors drawn on the GPU with PyTorch's seeded generator.
+
+    For sizes whose host-side draw would take too long (e.g. 1 GiB per rank);
+    the tests copy back only sampled values for the oracle.  Returns a list of
+    contiguous torch tensors (bf16 as torch.bfloat16, f32, i32).
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = []
+    for _ in range(P):
+        if dist == "uniform":
+            x = torch.rand(n, generator=g, device=device, dtype=torch.float32)
+            x.mul_(2.0).sub_(1.0)
+        elif dist == "normal":
+            x = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        elif dist == "int20":
+            x = torch.randint(-(2**20), 2**20 + 1, (n,), generator=g, device=device,
+                              dtype=torch.int32)
+        else:
+            raise ValueError(dist)
+        if dtype == "bf16":
+            x = x.to(torch.bfloat16)
+        elif dtype == "i32" and dist != "int20":
+            raise ValueError("float draws cannot fill int32 buffers")
+        out.append(x.contiguous())
+    return out

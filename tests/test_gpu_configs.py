@@ -1,0 +1,171 @@
+"""GPU parity at the full sizes of the benchmark workloads, default launch config.
+
+Workloads (seed 0, numpy PCG64, rank r = r-th draw):
+  AR-1   all-reduce sum, P=4 x 1,048,576 fp32 uniform[-1,1)    -> full oracle
+  RS-bf  reduce-scatter sum, P=8 x 67,108,864 bf16 normal(0,1) -> full oracle
+  RS-i   the same with int32 uniform in [-2^20, 2^20]           -> full oracle
+  AG     all-gather, P=8 x 16,777,216 bf16 normal(0,1)         -> oracle samples
+                                                                 + exact slot checks
+  AR-256 all-reduce sum, P=8 x 256 MiB bf16 uniform (the headline workload)
+                                                               -> oracle samples
+                                                                 + replica identity
+  sweep  all-reduce P=8, fp32/bf16, 4 KiB .. 1 GiB per rank in powers of 4,
+         sum/min/max, chunk 16 KiB .. 1 MiB                    -> full oracle up to
+                                                                 16 MiB per rank,
+                                                                 samples above
+The 1 GiB points draw their inputs on the GPU (PyTorch's seeded generator) and
+copy back only the sampled inputs for the oracle.
+"""
+from __future__ import annotations
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from _parity import assert_parity
+from collective_communication_plane_amd import ccl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NP = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+TORCH_BITS = {"f32": torch.int32, "bf16": torch.int16, "i32": torch.int32}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def up(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to(DEV)
+
+
+def down(t: torch.Tensor, dt) -> np.ndarray:
+    return t.view(torch.uint8).cpu().numpy().view(dt)
+
+
+def gather_at(ts, idx: np.ndarray, dt) -> list[np.ndarray]:
+    """Values of each device buffer at the sampled element indices."""
+    it = torch.from_numpy(idx.astype(np.int64)).to(DEV)
+    return [t.view(torch.uint8).view(TORCH_BITS[dt])[it].cpu().numpy().view(NP[dt]) for t in ts]
+
+
+def test_ar1_p4_1mi_fp32_full_oracle():
+    P, n = 4, 1_048_576
+    xs = si.rank_buffers(P, n, "f32", "uniform", seed=0)
+    dx = [up(x) for x in xs]
+    dy = [torch.empty_like(t) for t in dx]
+    ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM,
+                                 torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(xs, "f32", "sum")
+    for q in range(P):
+        n_neq = assert_parity(down(dy[q], np.float32), want[q], "f32", "sum", f"AR-1 q={q}")
+        print(f"AR-1 q={q}: non-bit-equal {n_neq}")
+
+
+@pytest.mark.parametrize("dtype,dist", [("bf16", "normal"), ("i32", "int20")])
+def test_rs_p8_64mi_full_oracle(dtype, dist):
+    P, N = 8, 67_108_864
+    M = N // P
+    xs = si.rank_buffers(P, N, dtype, dist, seed=0)
+    dx = [up(x) for x in xs]
+    dy = [torch.empty(M * xs[0].itemsize, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    ccl.check(ccl.ccl_reduce_scatter(dx, dy, P, M, ccl.DTYPES[dtype], ccl.CCL_SUM,
+                                     torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, dtype, "sum")
+    for s in range(P):
+        n_neq = assert_parity(down(dy[s], NP[dtype]), want[s], dtype, "sum", f"RS {dtype} s={s}")
+        print(f"RS {dtype} s={s}: non-bit-equal {n_neq}")
+
+
+def test_ag_p8_16mi_bf16():
+    P, M = 8, 16_777_216
+    xs = si.rank_buffers(P, M, "bf16", "normal", seed=0)
+    dx = [up(x) for x in xs]
+    dy = [torch.empty(P * M * 2, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    ccl.check(ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    # every slot of every output is byte-identical to the owner's input
+    for q in range(P):
+        for r in range(P):
+            assert torch.equal(dy[q][r * M * 2:(r + 1) * M * 2], dx[r]), (q, r)
+    # and sampled positions agree with the oracle's concatenation
+    idx = si.sample_indices(P * M, 100_000)
+    want = np.concatenate(xs)[idx.astype(np.int64)]
+    got = gather_at(dy, idx, "bf16")
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want)
+
+
+def _ar_sampled(ts_in, P, n, dtype, op, cfg=None, k=200_000, host_inputs=None):
+    outs = [torch.empty_like(t) for t in ts_in]
+    ccl.check(ccl.ccl_all_reduce(ts_in, outs, P, n, ccl.DTYPES[dtype], ccl.OPS[op],
+                                 torch.cuda.current_stream(), cfg))
+    torch.cuda.synchronize()
+    for q in range(1, P):
+        assert torch.equal(outs[q].view(torch.uint8), outs[0].view(torch.uint8)), q
+    idx = si.sample_indices(n, k)
+    if host_inputs is not None:
+        want = oracle.fold_at(host_inputs, dtype, op, idx)
+    else:
+        xin = gather_at(ts_in, idx, dtype)
+        want = oracle.fold_at(xin, dtype, op, np.arange(idx.size, dtype=np.uint64))
+    got = gather_at([outs[0]], idx, dtype)[0]
+    n_neq = assert_parity(got, want, dtype, op, f"AR n={n} {dtype} {op}")
+    del outs
+    return n_neq
+
+
+def test_ar_p8_256mib_bf16_headline():
+    P, n = 8, 134_217_728
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
+    dx = [up(x) for x in xs]
+    print("non-bit-equal:", _ar_sampled(dx, P, n, "bf16", "sum", host_inputs=xs))
+
+
+SWEEP_BYTES = [4096 * 4 ** k for k in range(10)]  # 4 KiB .. 1 GiB per rank
+
+
+@pytest.mark.parametrize("nbytes", SWEEP_BYTES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ar_sweep_sizes(nbytes, dtype):
+    P = 8
+    esz = 4 if dtype == "f32" else 2
+    n = nbytes // esz
+    ops = ["sum", "min", "max"] if nbytes <= 64 << 20 else ["sum"]
+    if nbytes <= 16 << 20:
+        xs = si.rank_buffers(P, n, dtype, "uniform", seed=0)
+        dx = [up(x) for x in xs]
+        for op in ops:
+            dy = [torch.empty_like(t) for t in dx]
+            ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.DTYPES[dtype], ccl.OPS[op],
+                                         torch.cuda.current_stream()))
+            torch.cuda.synchronize()
+            want = oracle.all_reduce(xs, dtype, op)[0]
+            for q in range(P):
+                assert_parity(down(dy[q], NP[dtype]), want, dtype, op, f"{nbytes}B {op} q={q}")
+    else:
+        dx = si.device_rank_buffers(P, n, dtype, "uniform", seed=0, device=DEV)
+        for op in ops:
+            _ar_sampled(dx, P, n, dtype, op)
+
+
+@pytest.mark.parametrize("chunk", [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10,
+                                   512 << 10, 1 << 20])
+@pytest.mark.parametrize("op", ["sum", "min", "max"])
+def test_ar_sweep_chunks(chunk, op):
+    P, n = 8, (64 << 20) // 2 + 3  # 64 MiB bf16 per rank plus a ragged tail
+    dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=1, device=DEV)
+    _ar_sampled(dx, P, n, "bf16", op, cfg=ccl.LaunchConfig(chunk_bytes=chunk), k=50_000)

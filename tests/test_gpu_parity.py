@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small and medium sizes (several chunks plus a ragged tail) are compared with
+the full oracle element by element; ragged counts, unaligned pointers, in-place
+forms, every launch-config knob and the guard bands around every buffer are
+covered.  Full-size configurations live in test_gpu_configs.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from _parity import DevBuf, assert_parity, upload_all
+from collective_communication_plane_amd import ccl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NP = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+ESZ = {"f32": 4, "bf16": 2, "i32": 4}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+    yield
+    torch.cuda.synchronize()
+
+
+def stream():
+    return torch.cuda.current_stream()
+
+
+def dist_of(dtype):
+    return "int20" if dtype == "i32" else "uniform"
+
+
+def run_ar(xs, dtype, op, offset=0, cfg=None, out_offset=None):
+    P, n = len(xs), xs[0].size
+    dx = upload_all(xs, DEV, offset)
+    dy = [DevBuf(n * ESZ[dtype], DEV, offset if out_offset is None else out_offset)
+          for _ in range(P)]
+    st = ccl.ccl_all_reduce([b.ptr for b in dx], [b.ptr for b in dy], P, n, ccl.DTYPES[dtype],
+                            ccl.OPS[op], stream(), cfg)
+    ccl.check(st, "all_reduce")
+    torch.cuda.synchronize()
+    for b in dx + dy:
+        assert b.guards_intact()
+    return [b.download(NP[dtype]) for b in dy]
+
+
+# ------------------------------------------------------------- all-reduce
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", ["sum", "min", "max"])
+def test_all_reduce_matches_oracle(P, dtype, op):
+    n = 3 * 16384 + 5  # several 64 KiB chunks plus a ragged tail
+    xs = si.rank_buffers(P, n, dtype, dist_of(dtype), seed=P * 7 + len(op))
+    got = run_ar(xs, dtype, op)
+    want = oracle.all_reduce(xs, dtype, op)
+    for q in range(P):
+        assert_parity(got[q], want[q], dtype, op, f"AR P={P} {dtype} {op} q={q}")
+        np.testing.assert_array_equal(got[q].view(np.uint8), got[0].view(np.uint8))
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 9, 4095, 4096, 4097, 65537])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_reduce_ragged_counts(n, dtype):
+    xs = si.rank_buffers(4, n, dtype, "uniform", seed=n)
+    got = run_ar(xs, dtype, "sum")
+    want = oracle.all_reduce(xs, dtype, "sum")
+    for q in range(4):
+        assert_parity(got[q], want[q], dtype, "sum", f"AR n={n}")
+
+
+@pytest.mark.parametrize("offset", [2, 4, 8, 12])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_reduce_unaligned_alike(offset, dtype):
+    if offset % ESZ[dtype]:
+        pytest.skip("pointer must be element-aligned")
+    xs = si.rank_buffers(3, 10001, dtype, "uniform", seed=offset)
+    got = run_ar(xs, dtype, "sum", offset=offset)
+    want = oracle.all_reduce(xs, dtype, "sum")
+    for q in range(3):
+        assert_parity(got[q], want[q], dtype, "sum", f"AR offset={offset}")
+
+
+def test_all_reduce_misaligned_relative_to_each_other():
+    """Inputs at offset 0, outputs at offset 4: the element-wise kernel runs."""
+    xs = si.rank_buffers(4, 5003, "f32", "uniform", seed=3)
+    got = run_ar(xs, "f32", "max", offset=0, out_offset=4)
+    want = oracle.all_reduce(xs, "f32", "max")
+    for q in range(4):
+        assert_parity(got[q], want[q], "f32", "max", "AR mixed alignment")
+
+
+def test_all_reduce_in_place():
+    P, n = 8, 20000
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=12)
+    bufs = upload_all(xs, DEV)
+    ptrs = [b.ptr for b in bufs]
+    ccl.check(ccl.ccl_all_reduce(ptrs, ptrs, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream()))
+    torch.cuda.synchronize()
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    for q in range(P):
+        assert bufs[q].guards_intact()
+        assert_parity(bufs[q].download(np.uint16), want[q], "bf16", "sum", "AR in place")
+
+
+def test_all_reduce_denormals_and_signed_zero():
+    tiny = np.array([1e-45, -1e-45, 1.1754942e-38, -0.0, 0.0, 3e-39, -2e-39, 5e-40],
+                    np.float32)
+    xs = [np.tile(tiny, 600), np.tile(tiny[::-1], 600), np.tile(tiny * np.float32(0.5), 600)]
+    for op in ("sum", "min", "max"):
+        got = run_ar(xs, "f32", op)
+        want = oracle.all_reduce(xs, "f32", op)
+        np.testing.assert_array_equal(got[0].view(np.uint32), want[0].view(np.uint32))
+    xb = [si.to_bf16_bits(x) for x in xs]
+    for op in ("sum", "min", "max"):
+        got = run_ar(xb, "bf16", op)
+        want = oracle.all_reduce(xb, "bf16", op)
+        np.testing.assert_array_equal(got[0], want[0])
+
+
+def test_bf16_rounding_ties_exercised():
+    """Pairs whose fp32 sum lands exactly halfway between bf16 values."""
+    base = si.rank_buffers(1, 8192, "bf16", "uniform", seed=77)[0]
+    f = si.bf16_bits_to_f32(base)
+    # x + x*2^-8 has a 1 in the first dropped bit: a tie for many x
+    half = si.to_bf16_bits(f * np.float32(2.0 ** -8))
+    xs = [base, half]
+    got = run_ar(xs, "bf16", "sum")
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    np.testing.assert_array_equal(got[0], want[0])
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(chunk_bytes=1024), dict(chunk_bytes=16384), dict(chunk_bytes=1 << 20),
+    dict(workgroups=1), dict(workgroups=7), dict(workgroups=1000),
+    dict(unroll=1), dict(unroll=2),
+    dict(nontemporal=1), dict(nontemporal=2), dict(nontemporal=3), dict(nontemporal=4),
+    dict(chunk_bytes=4096, workgroups=3, unroll=1, nontemporal=4),
+])
+def test_launch_config_does_not_change_results(cfg):
+    P, n = 8, 50001
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=5)
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    got = run_ar(xs, "bf16", "sum", cfg=ccl.LaunchConfig(**cfg))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want[q])
+    # reduce-scatter and all-gather under the same config
+    m = n // P + 3
+    xr = si.rank_buffers(P, P * m, "f32", "uniform", seed=6)
+    np.testing.assert_array_equal(np.concatenate(run_rs(xr, "f32", "min", cfg=ccl.LaunchConfig(**cfg))),
+                                  np.concatenate(oracle.reduce_scatter(xr, "f32", "min")))
+    xg = si.rank_buffers(P, m, "bf16", "normal", seed=7)
+    got = run_ag(xg, "bf16", cfg=ccl.LaunchConfig(**cfg))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
+
+
+# -------------------------------------------------------- reduce-scatter
+
+def run_rs(xs, dtype, op, offset=0, cfg=None, out_offset=None):
+    P = len(xs)
+    m = xs[0].size // P
+    dx = upload_all(xs, DEV, offset)
+    dy = [DevBuf(m * ESZ[dtype], DEV, offset if out_offset is None else out_offset)
+          for _ in range(P)]
+    ccl.check(ccl.ccl_reduce_scatter([b.ptr for b in dx], [b.ptr for b in dy], P, m,
+                                     ccl.DTYPES[dtype], ccl.OPS[op], stream(), cfg),
+              "reduce_scatter")
+    torch.cuda.synchronize()
+    for b in dx + dy:
+        assert b.guards_intact()
+    return [b.download(NP[dtype]) for b in dy]
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("op", ["sum", "min", "max"])
+@pytest.mark.parametrize("m", [1, 13, 3 * 8192 + 3])
+def test_reduce_scatter_matches_oracle(P, dtype, op, m):
+    xs = si.rank_buffers(P, P * m, dtype, dist_of(dtype), seed=P + m)
+    got = run_rs(xs, dtype, op)
+    want = oracle.reduce_scatter(xs, dtype, op)
+    for s in range(P):
+        assert_parity(got[s], want[s], dtype, op, f"RS P={P} m={m} s={s}")
+
+
+def test_reduce_scatter_unaligned_and_mixed():
+    xs = si.rank_buffers(4, 4 * 3001, "bf16", "uniform", seed=8)
+    want = oracle.reduce_scatter(xs, "bf16", "sum")
+    for off, ooff in [(2, 2), (6, 6), (0, 2), (4, 0)]:
+        got = run_rs(xs, "bf16", "sum", offset=off, out_offset=ooff)
+        for s in range(4):
+            assert_parity(got[s], want[s], "bf16", "sum", f"RS offsets {off}/{ooff}")
+
+
+def test_reduce_scatter_in_place_nccl_form():
+    P, m = 8, 4099
+    xs = si.rank_buffers(P, P * m, "f32", "uniform", seed=9)
+    bufs = upload_all(xs, DEV)
+    send = [b.ptr for b in bufs]
+    recv = [b.ptr + s * m * 4 for s, b in enumerate(bufs)]
+    ccl.check(ccl.ccl_reduce_scatter(send, recv, P, m, ccl.CCL_FLOAT32, ccl.CCL_SUM, stream()))
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, "f32", "sum")
+    for s in range(P):
+        got = bufs[s].download(np.float32)[s * m:(s + 1) * m]
+        assert_parity(got, want[s], "f32", "sum", "RS in place")
+
+
+# ------------------------------------------------------------ all-gather
+
+def run_ag(xs, dtype, offset=0, cfg=None, out_offset=None):
+    P, m = len(xs), xs[0].size
+    dx = upload_all(xs, DEV, offset)
+    dy = [DevBuf(P * m * ESZ[dtype], DEV, offset if out_offset is None else out_offset)
+          for _ in range(P)]
+    ccl.check(ccl.ccl_all_gather([b.ptr for b in dx], [b.ptr for b in dy], P, m,
+                                 ccl.DTYPES[dtype], stream(), cfg), "all_gather")
+    torch.cuda.synchronize()
+    for b in dx + dy:
+        assert b.guards_intact()
+    return [b.download(NP[dtype]) for b in dy]
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("m", [1, 9, 3 * 8192 + 1])
+def test_all_gather_matches_oracle(P, dtype, m):
+    xs = si.rank_buffers(P, m, dtype, dist_of(dtype), seed=P * m)
+    got = run_ag(xs, dtype)
+    want = oracle.all_gather(xs, dtype)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want[q])
+
+
+def test_all_gather_unaligned_and_mixed():
+    xs = si.rank_buffers(3, 2047, "bf16", "normal", seed=10)
+    want = oracle.all_gather(xs, "bf16")
+    for off, ooff in [(2, 2), (14, 14), (0, 6), (2, 0)]:
+        got = run_ag(xs, "bf16", offset=off, out_offset=ooff)
+        for q in range(3):
+            np.testing.assert_array_equal(got[q], want[q])
+
+
+def test_all_gather_in_place_nccl_form():
+    P, m = 8, 5000
+    xs = si.rank_buffers(P, m, "bf16", "normal", seed=11)
+    outs = [DevBuf(P * m * 2, DEV) for _ in range(P)]
+    for r in range(P):  # rank r's contribution sits in its own slot of its output
+        outs[r].base[outs[r].pad + r * m * 2: outs[r].pad + (r + 1) * m * 2].copy_(
+            torch.from_numpy(xs[r].view(np.uint8).copy()))
+    send = [o.ptr + r * m * 2 for r, o in enumerate(outs)]
+    ccl.check(ccl.ccl_all_gather(send, [o.ptr for o in outs], P, m, ccl.CCL_BFLOAT16, stream()))
+    torch.cuda.synchronize()
+    want = oracle.all_gather(xs, "bf16")
+    for q in range(P):
+        assert outs[q].guards_intact()
+        np.testing.assert_array_equal(outs[q].download(np.uint16), want[q])
+
+
+def test_rs_then_ag_equals_ar_on_gpu():
+    P, m = 8, 6151
+    xs = si.rank_buffers(P, P * m, "bf16", "uniform", seed=13)
+    rs = run_rs(xs, "bf16", "sum")
+    ag = run_ag(rs, "bf16")
+    ar = run_ar(xs, "bf16", "sum")
+    for q in range(P):
+        np.testing.assert_array_equal(ag[q], ar[q])
+
+
+# ------------------------------------------------------------- rejections
+
+def test_rejected_calls_touch_nothing():
+    P, n = 4, 1000
+    xs = si.rank_buffers(P, n, "f32", "uniform", seed=14)
+    dx = upload_all(xs, DEV)
+    dy = [DevBuf(n * 4, DEV) for _ in range(P)]
+    send = [b.ptr for b in dx]
+    recv = [b.ptr for b in dy]
+    bad_recv = recv[:1] + [recv[0] + 8] + recv[2:]  # two outputs overlap
+    assert ccl.ccl_all_reduce(send, bad_recv, P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM,
+                              stream()) == ccl.CCL_ERR_ALIASING
+    assert ccl.ccl_all_reduce(send, recv, P, n, ccl.CCL_FLOAT32, 9, stream()) == ccl.CCL_ERR_INVALID_ARG
+    assert ccl.ccl_all_reduce(send, recv, P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM, stream(),
+                              ccl.LaunchConfig(chunk_bytes=100)) == ccl.CCL_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    for b in dy:
+        assert (b.base == b.fill).all().item()

@@ -1,0 +1,302 @@
+"""Host-side tests of libccl without a GPU: exports, argument checks, planner.
+
+No compute call runs here.  Argument checks are exercised only on calls the
+library must reject before touching HIP, and the reshard planner (pure host
+code) is checked against the oracle's brute-force reshard by applying the
+planned byte intervals with numpy.
+"""
+from __future__ import annotations
+
+import itertools
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import synth_inputs as si
+from _golden import load_example
+from collective_communication_plane_amd import ccl
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ccl.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ccl_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "ccl_all_reduce" in names and "ccl_reshard_copy" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", ccl.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ccl._load()
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(ccl.EXPORTS) == set(names)
+
+
+def test_version_and_error_strings():
+    assert ccl.ccl_version() == 100
+    for code in range(7):
+        assert ccl.ccl_get_error_string(code)
+    assert ccl.ccl_get_error_string(99) == "unknown status"
+
+
+# ------------------------------------------------- argument checks (no HIP call)
+
+FAKE = 1 << 40  # never dereferenced: every call below is rejected first
+
+
+def ptrs(P, base=FAKE, stride=1 << 30):
+    return [base + r * stride for r in range(P)]
+
+
+@pytest.mark.parametrize("call", ["ar", "rs", "ag"])
+def test_rejects_bad_scalars(call):
+    def go(P=4, count=100, dtype=ccl.CCL_FLOAT32, op=ccl.CCL_SUM, send=None, recv=None, cfg=None):
+        send = ptrs(P) if send is None else send
+        recv = ptrs(P, base=FAKE * 2) if recv is None else recv
+        if call == "ar":
+            return ccl.ccl_all_reduce(send, recv, P, count, dtype, op, None, cfg)
+        if call == "rs":
+            return ccl.ccl_reduce_scatter(send, recv, P, count, dtype, op, None, cfg)
+        return ccl.ccl_all_gather(send, recv, P, count, dtype, None, cfg)
+
+    E = ccl.CCL_ERR_INVALID_ARG
+    assert go(P=0) == E
+    assert go(P=17) == E
+    assert go(dtype=7) == E
+    if call != "ag":
+        assert go(op=3) == E
+    assert go(send=[0, 0, 0, 0]) == E
+    assert go(recv=[FAKE * 2 + 2] + ptrs(3, base=FAKE * 3)) == E  # misaligned fp32
+    for bad in [dict(chunk_bytes=100), dict(chunk_bytes=1000), dict(workgroups=-1),
+                dict(stages=5), dict(unroll=3), dict(nontemporal=5),
+                dict(stages=2, chunk_bytes=1024 * 6)]:
+        assert go(cfg=ccl.LaunchConfig(**bad)) == E, bad
+    # count 0 is a no-op that never looks at the pointers
+    assert go(count=0, send=[0] * 4, recv=[0] * 4) == ccl.CCL_OK
+
+
+def test_rejects_aliasing():
+    P, n = 4, 1000
+    send = ptrs(P)
+    recv = ptrs(P, base=FAKE * 2)
+    A = ccl.CCL_ERR_ALIASING
+    # two outputs overlap
+    assert ccl.ccl_all_reduce(send, [recv[0], recv[0] + 64] + recv[2:], P, n, 0, 0) == A
+    # output shifted into an input
+    assert ccl.ccl_all_reduce(send, [send[0] + 4] + recv[1:], P, n, 0, 0) == A
+    # reduce-scatter: recv[1] inside send[1] but not on shard 1
+    assert ccl.ccl_reduce_scatter(send, [recv[0], send[1]] + recv[2:], P, n, 0, 0) == A
+    # all-gather: send[2] inside recv[0] but not on slot 2
+    assert ccl.ccl_all_gather([send[0], send[1], recv[0] + 4 * n * 1, send[3]], recv, P, n, 0) == A
+
+
+# ------------------------------------------------------------------ planner
+
+def plan_of(shape, dtype, src, dst):
+    return ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, dtype), ccl.make_mesh(src[0], src[1]),
+                                ccl.make_placements(src[2]), ccl.make_mesh(dst[0], dst[1]),
+                                ccl.make_placements(dst[2]))
+
+
+def apply_plan(plan, src_bufs, dst_sizes, esz):
+    """Execute a plan's intervals with numpy byte copies (host model of the copy)."""
+    src_b = [np.ascontiguousarray(b).view(np.uint8) for b in src_bufs]
+    dst_b = [np.full(n * esz, 0xEE, np.uint8) for n in dst_sizes]
+    written = [np.zeros(n * esz, np.int32) for n in dst_sizes]
+    ivs = ccl.plan_intervals(plan)
+    for iv in ivs:
+        st, reps = ccl.ccl_plan_shard_replicas(plan, iv.dst_shard)
+        assert st == 0 and len(reps) == iv.num_replicas
+        assert iv.leader in reps
+        seg = src_b[iv.src_rank - SRC_START[0]][iv.src_offset:iv.src_offset + iv.length]
+        assert seg.size == iv.length
+        for r in reps:
+            l = r - DST_START[0]
+            dst_b[l][iv.dst_offset:iv.dst_offset + iv.length] = seg
+            written[l][iv.dst_offset:iv.dst_offset + iv.length] += 1
+    return dst_b, written, ivs
+
+
+SRC_START = [0]
+DST_START = [0]
+
+
+def local_blocks(G, layout):
+    dims, _start, pl = layout
+    out = []
+    for c in itertools.product(*[range(m) for m in dims]):
+        blk = G
+        for k, p in enumerate(pl):
+            if p != "R":
+                blk = np.split(blk, dims[k], axis=p[1])[c[k]]
+        out.append(np.ascontiguousarray(blk).ravel())
+    return out
+
+
+def check_plan_against_oracle(shape, src, dst, dtype="bf16"):
+    G = si.tensor(shape, dtype, "w002", seed=len(shape))
+    src_bufs = local_blocks(G, src)
+    want = oracle.reshard(shape, src, dst, src_bufs)
+    st, plan = plan_of(shape, ccl.DTYPES[dtype], src, dst)
+    assert st == ccl.CCL_OK
+    try:
+        SRC_START[0], DST_START[0] = src[1], dst[1]
+        esz = G.itemsize
+        dst_b, written, ivs = apply_plan(plan, src_bufs, [w.size for w in want], esz)
+        for l, (b, w) in enumerate(zip(dst_b, want)):
+            np.testing.assert_array_equal(b.view(w.dtype), w)
+            assert np.all(written[l] == 1), "every destination byte written exactly once"
+        # no over-delivery: every shard reads exactly its own bytes once
+        n_shards = ccl.ccl_plan_num_dst_shards(plan)[1]
+        assert sum(iv.length for iv in ivs) == G.nbytes
+        assert sum(iv.length * iv.num_replicas for iv in ivs) == sum(w.nbytes for w in want)
+        # local sizes agree with the oracle's layouts
+        for l in range(oracle.mesh_size(src)):
+            assert ccl.ccl_plan_local_bytes(plan, 0, l) == (0, src_bufs[l].nbytes)
+        for l in range(oracle.mesh_size(dst)):
+            assert ccl.ccl_plan_local_bytes(plan, 1, l) == (0, want[l].nbytes)
+        # sorted by (shard, dst offset); leaders balanced within each shard
+        keys = [(iv.dst_shard, iv.dst_offset) for iv in ivs]
+        assert keys == sorted(keys)
+        for t in range(n_shards):
+            loads = {}
+            reps = ccl.ccl_plan_shard_replicas(plan, t)[1]
+            for iv in ivs:
+                if iv.dst_shard == t:
+                    loads[iv.leader] = loads.get(iv.leader, 0) + 1
+            counts = [loads.get(r, 0) for r in reps]
+            assert max(counts) - min(counts) <= 1
+        # maximal runs: no two consecutive intervals could merge
+        for a, b in zip(ivs, ivs[1:]):
+            if a.dst_shard == b.dst_shard and a.src_rank == b.src_rank:
+                assert not (a.dst_offset + a.length == b.dst_offset and
+                            a.src_offset + a.length == b.src_offset)
+        return ivs
+    finally:
+        assert ccl.ccl_plan_destroy(plan) == ccl.CCL_OK
+
+
+@pytest.mark.parametrize("name", ["example_a.txt", "example_b.txt"])
+def test_planner_worked_examples(name):
+    ex = load_example(name)
+    shape = ex["shape"]
+    G = np.arange(int(np.prod(shape)), dtype=np.int32).reshape(shape)
+    src_bufs = []
+    for l in range(oracle.mesh_size(ex["src"])):
+        (r0, r1), (c0, c1) = ex["hold"]["src"][ex["src"][1] + l]
+        src_bufs.append(np.ascontiguousarray(G[r0:r1, c0:c1]).ravel())
+    st, plan = plan_of(shape, ccl.CCL_INT32, ex["src"], ex["dst"])
+    assert st == 0
+    try:
+        SRC_START[0], DST_START[0] = ex["src"][1], ex["dst"][1]
+        sizes = [oracle.local_numel(shape, ex["dst"])] * oracle.mesh_size(ex["dst"])
+        dst_b, written, _ = apply_plan(plan, src_bufs, sizes, 4)
+        for l, b in enumerate(dst_b):
+            (r0, r1), (c0, c1) = ex["hold"]["dst"][ex["dst"][1] + l]
+            np.testing.assert_array_equal(b.view(np.int32), G[r0:r1, c0:c1].ravel())
+    finally:
+        ccl.ccl_plan_destroy(plan)
+
+
+def _layouts(ndim, shape):
+    meshes = [[1], [2], [3], [4], [2, 2], [1, 3], [3, 1], [2, 3]]
+    for dims in meshes:
+        choices = [["R"] + [("S", d) for d in range(ndim)] for _ in dims]
+        for pl in itertools.product(*choices):
+            if sum(p != "R" for p in pl) > 1:
+                continue
+            if all(p == "R" or shape[p[1]] % dims[k] == 0 for k, p in enumerate(pl)):
+                yield dims, list(pl)
+
+
+@pytest.mark.parametrize("shape", [(6,), (4, 6), (2, 3, 4), (6, 1, 4)])
+def test_planner_against_oracle_on_tiny_layouts(shape):
+    layouts = list(_layouts(len(shape), shape))
+    rng = np.random.default_rng(sum(shape))
+    pairs = [(a, b) for a in layouts for b in layouts]
+    for i in rng.choice(len(pairs), size=min(250, len(pairs)), replace=False):
+        (sd, spl), (dd, dpl) = pairs[i]
+        src = (sd, 0, spl)
+        dst = (dd, int(np.prod(sd)), dpl)
+        check_plan_against_oracle(shape, src, dst)
+
+
+def test_planner_weight_reshard_closed_forms():
+    """[8192, 28672] bf16, Mesh([1,4]) [R,S(0)] -> Mesh([2,2],4) [R,S(0)]:
+    source rank r fills half r % 2 of destination shard r // 2, whose replicas
+    are ranks {4, 6} and {5, 7}."""
+    st, plan = plan_of((8192, 28672), ccl.CCL_BFLOAT16, ([1, 4], 0, ["R", ("S", 0)]),
+                       ([2, 2], 4, ["R", ("S", 0)]))
+    assert st == 0
+    try:
+        ivs = ccl.plan_intervals(plan)
+        blk = 2048 * 28672 * 2
+        assert [(iv.src_rank, iv.dst_shard, iv.src_offset, iv.dst_offset, iv.length) for iv in ivs] == \
+            [(r, r // 2, 0, (r % 2) * blk, blk) for r in range(4)]
+        assert ccl.ccl_plan_shard_replicas(plan, 0)[1] == [4, 6]
+        assert ccl.ccl_plan_shard_replicas(plan, 1)[1] == [5, 7]
+        assert sorted(iv.leader for iv in ivs) == [4, 5, 6, 7]
+    finally:
+        ccl.ccl_plan_destroy(plan)
+
+
+def test_planner_moe_reshard_closed_forms():
+    """[64, 2048, 1408] bf16, Shard(0) over 8 -> Shard(1) over 4: expert e's
+    rows [512d, 512d+512) go from rank e // 8 to rank 8 + d."""
+    st, plan = plan_of((64, 2048, 1408), ccl.CCL_BFLOAT16, ([8], 0, [("S", 0)]),
+                       ([4], 8, [("S", 1)]))
+    assert st == 0
+    try:
+        ivs = ccl.plan_intervals(plan)
+        assert len(ivs) == 256
+        row = 1408 * 2
+        want = sorted((d, e * 512 * row, e // 8, ((e % 8) * 2048 + 512 * d) * row)
+                      for d in range(4) for e in range(64))
+        got = [(iv.dst_shard, iv.dst_offset, iv.src_rank, iv.src_offset) for iv in ivs]
+        assert got == want
+        assert all(iv.length == 512 * row for iv in ivs)
+    finally:
+        ccl.ccl_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("shape,src,dst,code", [
+    ((8,), ([2], 0, [("S", 0)]), ([2], 1, ["R"]), ccl.CCL_ERR_LAYOUT),        # meshes overlap
+    ((9,), ([2], 0, [("S", 0)]), ([1], 2, ["R"]), ccl.CCL_ERR_LAYOUT),        # uneven split
+    ((8, 8), ([2, 2], 0, [("S", 0), ("S", 1)]), ([1], 4, ["R"]), ccl.CCL_ERR_LAYOUT),  # 2 shard axes
+    ((8,), ([65], 0, ["R"]), ([1], 65, ["R"]), ccl.CCL_ERR_LAYOUT),           # mesh too large
+    ((8,), ([2], 0, [("S", 1)]), ([1], 2, ["R"]), ccl.CCL_ERR_INVALID_ARG),   # no dim 1
+    ((8,), ([0], 0, ["R"]), ([1], 2, ["R"]), ccl.CCL_ERR_INVALID_ARG),        # empty axis
+    ((8,), ([2], -1, ["R"]), ([1], 2, ["R"]), ccl.CCL_ERR_INVALID_ARG),       # negative rank
+])
+def test_planner_rejects_invalid_layouts(shape, src, dst, code):
+    st, plan = plan_of(shape, ccl.CCL_FLOAT32, src, dst)
+    assert st == code and plan is None
+
+
+def test_planner_regrow_is_independent():
+    """Planning for one mesh and then for a larger one gives two valid,
+    independent plans (a grown communicator is just a new plan)."""
+    a = check_plan_against_oracle((8, 12), ([2], 0, [("S", 0)]), ([2], 2, [("S", 1)]))
+    b = check_plan_against_oracle((8, 12), ([2], 0, [("S", 0)]), ([2, 2], 2, [("S", 1), "R"]))
+    assert len(a) == len(b)
+
+
+def test_planner_empty_tensor():
+    st, plan = plan_of((0, 16), ccl.CCL_FLOAT32, ([2], 0, [("S", 1)]), ([2], 2, ["R"]))
+    assert st == 0
+    try:
+        assert ccl.ccl_plan_num_intervals(plan) == (0, 0)
+        assert ccl.ccl_reshard_copy(plan, [0, 0], [0, 0]) == ccl.CCL_OK
+    finally:
+        ccl.ccl_plan_destroy(plan)
