@@ -16,7 +16,17 @@ Besides the headline value the line carries:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (single thread);
   rows          the other data-plane workloads (reduce-scatter bf16 and int32,
-                all-gather, the two weight reshards), each timed the same way.
+                all-gather, the all-reduce through the LDS pipeline, the two
+                weight reshards), each timed the same way after a warmup of
+                at least half a second.
+
+Other modes:
+  --sweep       the launch-configuration sweep (chunk bytes, stages, unroll,
+                resident workgroups per CU) for all-reduce, reduce-scatter
+                and all-gather at P=8 x 256 MiB bf16; one JSON line per point.
+  --calibrate   also runs a plain 1 GiB device copy (torch) a few times, the
+                known-size reference that scales rocprofv3's FETCH_SIZE and
+                WRITE_SIZE counters to bytes.
 """
 from __future__ import annotations
 
@@ -62,12 +72,17 @@ def read_traffic(bytes_per_launch_alg: float):
         return None
 
 
-def timed(launch, steps: int, warmup: int, stream):
+def timed(launch, steps: int, warmup: int, stream, min_warm_s: float = 0.0):
     import torch
 
     for _ in range(warmup):
         launch()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:  # let the clocks ramp up
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -109,7 +124,7 @@ def cpu_baseline(seconds: float = 10.0):
                       f"one thread"}
 
 
-def rows(dev, stream, steps: int, warmup: int):
+def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     import numpy as np
     import torch
 
@@ -132,7 +147,7 @@ def rows(dev, stream, steps: int, warmup: int):
         esz = dx[0].numel() // N
         dy = [torch.empty(M * esz, dtype=torch.uint8, device=dev) for _ in range(P)]
         ms = timed(lambda: ccl.check(ccl.ccl_reduce_scatter(dx, dy, P, M, code, ccl.CCL_SUM, stream)),
-                   steps, warmup, stream)
+                   steps, warmup, stream, warm_s)
         record(f"reduce_scatter_{dt}", P * N * esz + P * M * esz, ms,
                f"reduce_scatter sum, P=8 x 67,108,864 {dt}")
         del dx, dy
@@ -144,8 +159,21 @@ def rows(dev, stream, steps: int, warmup: int):
     del xs
     dy = [torch.empty(P * M * 2, dtype=torch.uint8, device=dev) for _ in range(P)]
     ms = timed(lambda: ccl.check(ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, stream)),
-               steps, warmup, stream)
+               steps, warmup, stream, warm_s)
     record("all_gather_bf16", P * M * 2 + P * P * M * 2, ms, "all_gather, P=8 x 16,777,216 bf16")
+    del dx, dy
+    torch.cuda.empty_cache()
+
+    # the headline all-reduce again, through the LDS pipeline instead of VGPRs
+    n = 134_217_728
+    dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
+    dy = [torch.empty_like(t) for t in dx]
+    lds_cfg = ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=2)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                                    stream, lds_cfg)), steps, warmup, stream, warm_s)
+    record("all_reduce_bf16_lds_pipeline", 2 * P * n * 2, ms,
+           "all_reduce sum, P=8 x 134,217,728 bf16, LDS pipeline (2 stages, 4 KiB chunks, "
+           "<= 2 workgroups per CU)")
     del dx, dy
     torch.cuda.empty_cache()
 
@@ -170,7 +198,7 @@ def rows(dev, stream, steps: int, warmup: int):
                                         ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))
         ccl.check(st, "reshard_plan")
         ms = timed(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream)), steps,
-                   warmup, stream)
+                   warmup, stream, warm_s)
         ccl.check(ccl.ccl_plan_destroy(plan))
         record(name, tensor_bytes * (1 + rho), ms,
                f"reshard {list(shape)} bf16 {src} -> {dst}")
@@ -179,14 +207,69 @@ def rows(dev, stream, steps: int, warmup: int):
     return out
 
 
+def sweep(dev, stream) -> None:
+    """Launch-configuration sweep at P=8 x 256 MiB bf16 (sum); one JSON line each."""
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    P, n = 8, 134_217_728
+    dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
+    dy = [torch.empty(n * 2, dtype=torch.uint8, device=dev) for _ in range(P)]
+    ops = {
+        "all_reduce": (lambda c: ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                                    stream, c), 2 * P * n * 2),
+        "reduce_scatter": (lambda c: ccl.ccl_reduce_scatter(dx, dy, P, n // P, ccl.CCL_BFLOAT16,
+                                                            ccl.CCL_SUM, stream, c),
+                           P * n * 2 + n * 2),
+        "all_gather": (lambda c: ccl.ccl_all_gather(dx, dy, P, n // P, ccl.CCL_BFLOAT16, stream, c),
+                       n * 2 + P * n * 2),
+    }
+    points = [None]
+    for occ in (1, 2, 3, 4, 32):
+        for chunk in (4096, 8192, 16384, 65536):
+            for unroll in (1, 2, 4):
+                if chunk >= 4096 * unroll:
+                    points.append(dict(chunk_bytes=chunk, unroll=unroll, stages=1, occupancy=occ))
+            for stages in (2, 3, 4):
+                points.append(dict(chunk_bytes=chunk, stages=stages, occupancy=occ))
+    for name, (fn, nbytes) in ops.items():
+        best = None
+        for pt in points:
+            c = ccl.LaunchConfig(**pt) if pt else None
+            ms = timed(lambda: ccl.check(fn(c), name), 20, 3, stream, 0.05)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rec = {"sweep": name, "config": pt or "default", "ms": round(ms, 5),
+                   "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            print(json.dumps(rec), flush=True)
+            if best is None or gbs > best["GB/s"]:
+                best = rec
+        print(json.dumps({"sweep_best": name, **best}), flush=True)
+
+
+def calibrate(dev) -> None:
+    """A plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB)."""
+    import torch
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--row-steps", type=int, default=50)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--calibrate", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -206,6 +289,11 @@ def main() -> int:
     ccl._load()  # fails loudly if libccl.so is missing
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
+    if args.sweep:
+        sweep(dev, stream)
+        return 0
+    if args.calibrate:
+        calibrate(dev)
 
     P, n = 8, 134_217_728
     xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
@@ -249,7 +337,8 @@ def main() -> int:
             "workload": "all_reduce sum, P=8 rank buffers x 134,217,728 bf16 (256 MiB) each, "
                         "uniform[-1,1) seed 0, fp32 fold in rank order, bf16 out",
             "P": P, "count": n, "storage_dtype": "bf16", "accumulate": "f32",
-            "hbm_bytes_per_step": bytes_per_step, "launch": "library defaults",
+            "hbm_bytes_per_step": bytes_per_step,
+            "launch": "library defaults (register-direct, 4 KiB chunks, <= 3 workgroups per CU)",
             "parity_spot_check": parity,
         },
         "roofline": {

@@ -61,8 +61,13 @@ int device_cu_count(int dev) {
   return cached[dev];
 }
 
-ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out) {
-  Launch l{kDefaultChunkBytes, 0, 1, 2, true, true};
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, Launch *out) {
+  const OpDefaults &d = op == OP_AR   ? kDefaultsAR
+                        : op == OP_RS ? kDefaultsRS
+                        : op == OP_AG ? kDefaultsAG
+                                      : kDefaultsReshard;
+  Launch l{d.chunk_bytes, 0, d.stages, d.unroll, true, true, d.occupancy};
+  bool explicit_stages = false;
   if (cfg) {
     if (cfg->chunk_bytes) {
       if (cfg->chunk_bytes % kVecBytes || cfg->chunk_bytes < 1024 ||
@@ -73,8 +78,11 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out) {
     if (cfg->workgroups < 0 || cfg->workgroups > (1 << 24)) return CCL_ERR_INVALID_ARG;
     l.workgroups = cfg->workgroups;
     if (cfg->stages < 0 || cfg->stages > 4) return CCL_ERR_INVALID_ARG;
-    if (cfg->stages) l.stages = cfg->stages;
-    if (cfg->unroll < 0 || cfg->unroll > 2) return CCL_ERR_INVALID_ARG;
+    if (cfg->stages) {
+      l.stages = cfg->stages;
+      explicit_stages = true;
+    }
+    if (cfg->unroll < 0 || cfg->unroll > 4 || cfg->unroll == 3) return CCL_ERR_INVALID_ARG;
     if (cfg->unroll) l.unroll = cfg->unroll;
     if (cfg->nontemporal < 0 || cfg->nontemporal > 4) return CCL_ERR_INVALID_ARG;
     if (cfg->nontemporal == 4) {
@@ -83,7 +91,13 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out) {
       l.nt_load = cfg->nontemporal & 1;
       l.nt_store = (cfg->nontemporal >> 1) & 1;
     }
-    if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) return CCL_ERR_INVALID_ARG;
+    if (cfg->occupancy < 0 || cfg->occupancy > 32 || cfg->reserved != 0) return CCL_ERR_INVALID_ARG;
+    if (cfg->occupancy) l.occupancy = cfg->occupancy;
+  }
+  if (op == OP_RESHARD && explicit_stages && l.stages != 1) return CCL_ERR_UNSUPPORTED;
+  if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) {
+    if (explicit_stages) return CCL_ERR_INVALID_ARG;
+    l.stages = 1;
   }
   *out = l;
   return CCL_OK;
@@ -111,7 +125,7 @@ int ccl_version(void) { return 100; }
 ccl_status_t ccl_all_reduce(const void *const *send, void *const *recv, int nranks, size_t count,
                             int dtype, int op, void *stream, const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AR, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
     return CCL_ERR_INVALID_ARG;
@@ -137,7 +151,7 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
                                 size_t recvcount, int dtype, int op, void *stream,
                                 const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RS, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
     return CCL_ERR_INVALID_ARG;
@@ -163,7 +177,7 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
                             size_t sendcount, int dtype, void *stream,
                             const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AG, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0) return CCL_ERR_INVALID_ARG;
   if (sendcount == 0) return CCL_OK;
@@ -188,7 +202,7 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
                               void *const *dst_bufs, void *stream,
                               const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD, &l);
   if (st) return st;
   if (!plan || !src_bufs || !dst_bufs) return CCL_ERR_INVALID_ARG;
   ccl_plan *p = const_cast<ccl_plan *>(plan);
@@ -212,7 +226,6 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
     }
   }
   if (p->intervals.empty()) return CCL_OK;
-  if (l.stages != 1) return CCL_ERR_UNSUPPORTED;  // the copy has no LDS pipeline
   return ccl::reshard_launch(p, src_bufs, dst_bufs, l, (hipStream_t)stream);
 }
 

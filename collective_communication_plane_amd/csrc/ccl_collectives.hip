@@ -177,45 +177,317 @@ __global__ void __launch_bounds__(kThreads) coll_scalar_kernel(CollArgs a, int n
   }
 }
 
+// ------------------------------------------------------------ LDS pipeline
+//
+// The staged form of the same fold ([digest] s2.3: each task becomes a series
+// of windows fed through a multi-stage shared-memory pipeline, driven by
+// asynchronous bulk loads with completion barriers).  On gfx950 the bulk load
+// is global_load_lds_dwordx4, which moves 16 bytes per lane from HBM straight
+// into LDS without touching VGPRs, and the completion barrier is the
+// producer's s_waitcnt vmcnt followed by s_barrier.
+//
+// A workgroup is 4 consumer waves plus 4 producer waves.  The ring has S
+// stages; a stage holds one 4 KiB tile of every input (the tile is 256
+// vectors: one per consumer lane).  Producer wave p loads row p (64 vectors)
+// of each input's tile; consumer wave w folds row w.  Per tile j:
+//   producer: issue tile j+S-1 into the stage tile j-1 used, wait until tile
+//             j has landed, barrier A_j, barrier B_j
+//   consumer: barrier A_j, read stage j%S and fold, barrier B_j, store
+// so up to S-1 tiles are in flight while a tile is folded and stored.  Every
+// producer issues exactly one load per input per tile (lanes past the end of
+// a chunk re-read its last vector, so the count of outstanding loads is exact
+// and no load leaves the buffers).
+
+constexpr int kLdsWaves = 4;                   // consumer waves = producer waves
+constexpr int kLdsThreads = 2 * kLdsWaves * 64;
+constexpr int kTileVecs = kLdsWaves * 64;      // vectors per input per tile
+
+// s_waitcnt with only the vector-memory counter limited to n (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void waitcnt_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int N = 0>
+__device__ __forceinline__ void waitcnt_vm_le(int n) {
+  if constexpr (N < 63) {
+    if (n <= N) {
+      waitcnt_vm<N>();
+      return;
+    }
+    waitcnt_vm_le<N + 1>(n);
+  } else {
+    waitcnt_vm<63>();
+  }
+}
+
+__device__ __forceinline__ void lgkm_wait_all() {
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Walks a workgroup's chunks tile by tile (both roles walk the same sequence).
+struct TileCursor {
+  uint64_t c;       // current chunk
+  uint64_t t;       // tile inside the chunk
+  uint64_t v0, v1;  // vector range of the chunk
+  int s;            // segment
+  bool valid;
+};
+
+__device__ __forceinline__ void cursor_chunk(const CollArgs &a, TileCursor &k) {
+  for (; k.c < a.total_chunks; k.c += gridDim.x) {
+    k.s = (int)(k.c / a.chunks_per_seg);
+    const uint64_t lc = k.c - (uint64_t)k.s * a.chunks_per_seg;
+    k.v0 = lc * a.chunk_vecs;
+    k.v1 = min(k.v0 + a.chunk_vecs, a.nvec[k.s]);
+    k.t = 0;
+    if (k.v1 > k.v0) {
+      k.valid = true;
+      return;
+    }
+  }
+  k.valid = false;
+}
+
+__device__ __forceinline__ void cursor_begin(const CollArgs &a, TileCursor &k) {
+  k.c = blockIdx.x;
+  cursor_chunk(a, k);
+}
+
+__device__ __forceinline__ void cursor_next(const CollArgs &a, TileCursor &k) {
+  ++k.t;
+  if (k.v0 + k.t * kTileVecs >= k.v1) {
+    k.c += gridDim.x;
+    cursor_chunk(a, k);
+  }
+}
+
+template <int KIND, int DT, int OP, int PMAX, int S>
+__global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
+  constexpr int esz = DT == CCL_BFLOAT16 ? 2 : 4;
+  constexpr int V = kVecBytes / esz;
+  constexpr int NI = KIND == KIND_AG ? 1 : PMAX;
+  constexpr int NO = KIND == KIND_RS ? 1 : PMAX;
+  constexpr int kTileBytes = kTileVecs * kVecBytes;
+  constexpr int kStageBytes = NI * kTileBytes;
+  __shared__ __attribute__((aligned(16))) char lds[S * kStageBytes];
+
+  const int P = a.P;
+  const int ni = KIND == KIND_AG ? 1 : P;
+  const int no = KIND == KIND_RS ? 1 : P;
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+
+  if (wave >= kLdsWaves) {
+    // ---------------------------------------------------------- producer
+    const int p = wave - kLdsWaves;
+    TileCursor issue;
+    cursor_begin(a, issue);
+    TileCursor need = issue;
+    int inflight = 0;  // tiles issued and not yet waited for
+    auto issue_tile = [&](const TileCursor &k, int stage) {
+      const uint64_t head = a.head[k.s];
+      uint64_t vv = k.v0 + k.t * kTileVecs + (uint64_t)p * 64 + lane;
+      if (vv >= k.v1) vv = k.v1 - 1;
+      char *dst = lds + stage * kStageBytes + p * 64 * kVecBytes;
+      if (ntl) {
+#pragma unroll
+        for (int r = 0; r < NI; ++r)
+          if (r < ni)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(in_at<KIND>(a, k.s, r, head, esz) + vv * kVecBytes),
+                (__attribute__((address_space(3))) void *)(dst + r * kTileBytes), kVecBytes, 0, 2);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NI; ++r)
+          if (r < ni)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(in_at<KIND>(a, k.s, r, head, esz) + vv * kVecBytes),
+                (__attribute__((address_space(3))) void *)(dst + r * kTileBytes), kVecBytes, 0, 0);
+      }
+    };
+    int stage_issue = 0;
+    for (int j = 0; j < S - 1 && issue.valid; ++j) {
+      issue_tile(issue, stage_issue);
+      stage_issue = stage_issue + 1 == S ? 0 : stage_issue + 1;
+      ++inflight;
+      cursor_next(a, issue);
+    }
+    while (need.valid) {
+      if (issue.valid) {
+        issue_tile(issue, stage_issue);
+        stage_issue = stage_issue + 1 == S ? 0 : stage_issue + 1;
+        ++inflight;
+        cursor_next(a, issue);
+      }
+      // tile `need` is the oldest in flight: allow the younger ones to pend
+      waitcnt_vm_le((inflight - 1) * ni);
+      --inflight;
+      wg_barrier();  // A: the tile has landed
+      wg_barrier();  // B: consumers have read it
+      cursor_next(a, need);
+    }
+  } else {
+    // ---------------------------------------------------------- consumer
+    const int w = wave;
+    // Scalar head and tail of each segment, by the workgroup that owns the
+    // segment's first chunk (also when the segment has no whole vector).
+    for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
+      const int s = (int)(c / a.chunks_per_seg);
+      if (c - (uint64_t)s * a.chunks_per_seg != 0) continue;
+      const uint64_t head = a.head[s];
+      const uint64_t tail0 = head + a.nvec[s] * V;
+      const uint64_t ntail = a.seg_elems - tail0;
+      const uint64_t t = threadIdx.x;
+      if (t < head) scalar_element<KIND, DT, OP>(a, s, t);
+      else if (t - head < ntail) scalar_element<KIND, DT, OP>(a, s, tail0 + (t - head));
+    }
+    TileCursor k;
+    cursor_begin(a, k);
+    int stage = 0;
+    while (k.valid) {
+      const int s = k.s;
+      const uint64_t head = a.head[s];
+      const uint64_t vv = k.v0 + k.t * kTileVecs + (uint64_t)w * 64 + lane;
+      wg_barrier();  // A
+      u32x4 x[NI];
+      const char *src = lds + stage * kStageBytes + (w * 64 + lane) * kVecBytes;
+#pragma unroll
+      for (int r = 0; r < NI; ++r)
+        if (r < ni) x[r] = *(const u32x4 *)(src + r * kTileBytes);
+      lgkm_wait_all();
+      wg_barrier();  // B
+      stage = stage + 1 == S ? 0 : stage + 1;
+      if (vv < k.v1) {
+        u32x4 y;
+        if constexpr (KIND == KIND_AG) y = x[0];
+        else y = fold_vec<DT, OP, NI>(x, ni);
+#pragma unroll
+        for (int q = 0; q < NO; ++q)
+          if (q < no) {
+            char *d = out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes;
+            if (nts) st_nt(d, y);
+            else st_plain(d, y);
+          }
+      }
+      cursor_next(a, k);
+    }
+  }
+}
+
+// Largest stage count that keeps the ring within 128 KiB of LDS.
+inline int lds_stages(int stages, int ni_max) {
+  const int per_stage = ni_max * kTileVecs * kVecBytes;
+  int s = stages;
+  while (s > 2 && s * per_stage > 128 * 1024) --s;
+  return s;
+}
+
 // ------------------------------------------------------------- dispatch
 
 template <int KIND, int DT, int OP, int PMAX>
-hipError_t launch_vec(const CollArgs &a, int unroll, unsigned grid, hipStream_t st) {
+hipError_t launch_vec(const CollArgs &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
   if (unroll == 1)
-    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 1>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 1>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (unroll == 2 || PMAX > 8)
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 2>), dim3(grid), dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 2>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 4>), dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
 template <int KIND, int DT, int OP>
-hipError_t launch_pmax(const CollArgs &a, int unroll, unsigned grid, hipStream_t st) {
-  if (a.P <= 4) return launch_vec<KIND, DT, OP, 4>(a, unroll, grid, st);
-  if (a.P <= 8) return launch_vec<KIND, DT, OP, 8>(a, unroll, grid, st);
-  return launch_vec<KIND, DT, OP, 16>(a, unroll, grid, st);
+hipError_t launch_pmax(const CollArgs &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
+  if (a.P <= 4) return launch_vec<KIND, DT, OP, 4>(a, unroll, grid, lds, st);
+  if (a.P <= 8) return launch_vec<KIND, DT, OP, 8>(a, unroll, grid, lds, st);
+  return launch_vec<KIND, DT, OP, 16>(a, unroll, grid, lds, st);
 }
 
 template <int KIND, int DT>
-hipError_t launch_op(const CollArgs &a, int op, int unroll, unsigned grid, hipStream_t st) {
+hipError_t launch_op(const CollArgs &a, int op, int unroll, unsigned grid, size_t lds,
+                     hipStream_t st) {
   switch (op) {
-    case CCL_SUM: return launch_pmax<KIND, DT, CCL_SUM>(a, unroll, grid, st);
-    case CCL_MIN: return launch_pmax<KIND, DT, CCL_MIN>(a, unroll, grid, st);
-    default: return launch_pmax<KIND, DT, CCL_MAX>(a, unroll, grid, st);
+    case CCL_SUM: return launch_pmax<KIND, DT, CCL_SUM>(a, unroll, grid, lds, st);
+    case CCL_MIN: return launch_pmax<KIND, DT, CCL_MIN>(a, unroll, grid, lds, st);
+    default: return launch_pmax<KIND, DT, CCL_MAX>(a, unroll, grid, lds, st);
   }
 }
 
 template <int KIND>
-hipError_t launch_dt(const CollArgs &a, int dt, int op, int unroll, unsigned grid, hipStream_t st) {
+hipError_t launch_dt(const CollArgs &a, int dt, int op, int unroll, unsigned grid, size_t lds,
+                     hipStream_t st) {
   if constexpr (KIND == KIND_AG) {
     // A copy: only the element size matters.
-    if (dt == CCL_BFLOAT16) return launch_pmax<KIND, CCL_BFLOAT16, CCL_SUM>(a, unroll, grid, st);
-    return launch_pmax<KIND, CCL_INT32, CCL_SUM>(a, unroll, grid, st);
+    if (dt == CCL_BFLOAT16) return launch_pmax<KIND, CCL_BFLOAT16, CCL_SUM>(a, unroll, grid, lds, st);
+    return launch_pmax<KIND, CCL_INT32, CCL_SUM>(a, unroll, grid, lds, st);
   } else {
     switch (dt) {
-      case CCL_FLOAT32: return launch_op<KIND, CCL_FLOAT32>(a, op, unroll, grid, st);
-      case CCL_BFLOAT16: return launch_op<KIND, CCL_BFLOAT16>(a, op, unroll, grid, st);
-      default: return launch_op<KIND, CCL_INT32>(a, op, unroll, grid, st);
+      case CCL_FLOAT32: return launch_op<KIND, CCL_FLOAT32>(a, op, unroll, grid, lds, st);
+      case CCL_BFLOAT16: return launch_op<KIND, CCL_BFLOAT16>(a, op, unroll, grid, lds, st);
+      default: return launch_op<KIND, CCL_INT32>(a, op, unroll, grid, lds, st);
     }
+  }
+}
+
+template <int KIND, int DT, int OP, int PMAX>
+hipError_t launch_lds_s(const CollArgs &a, int stages, int occupancy, unsigned grid,
+                        hipStream_t st) {
+  constexpr int NI = KIND == KIND_AG ? 1 : PMAX;
+  constexpr size_t kStage = (size_t)NI * kTileVecs * kVecBytes;
+  const int s = lds_stages(stages, NI);
+  if constexpr (kStage * 3 <= 128 * 1024) {
+    if (s == 4 && kStage * 4 <= 128 * 1024)
+      hipLaunchKernelGGL((coll_lds_kernel<KIND, DT, OP, PMAX, 4>), dim3(grid), dim3(kLdsThreads),
+                         occupancy_lds(occupancy, 4 * kStage), st, a);
+    else if (s >= 3)
+      hipLaunchKernelGGL((coll_lds_kernel<KIND, DT, OP, PMAX, 3>), dim3(grid), dim3(kLdsThreads),
+                         occupancy_lds(occupancy, 3 * kStage), st, a);
+    else
+      hipLaunchKernelGGL((coll_lds_kernel<KIND, DT, OP, PMAX, 2>), dim3(grid), dim3(kLdsThreads),
+                         occupancy_lds(occupancy, 2 * kStage), st, a);
+  } else {
+    (void)s;
+    hipLaunchKernelGGL((coll_lds_kernel<KIND, DT, OP, PMAX, 2>), dim3(grid), dim3(kLdsThreads),
+                       occupancy_lds(occupancy, 2 * kStage), st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int KIND, int DT, int OP>
+hipError_t launch_lds_p(const CollArgs &a, int stages, int occ, unsigned grid, hipStream_t st) {
+  if (a.P <= 4) return launch_lds_s<KIND, DT, OP, 4>(a, stages, occ, grid, st);
+  if (a.P <= 8) return launch_lds_s<KIND, DT, OP, 8>(a, stages, occ, grid, st);
+  return launch_lds_s<KIND, DT, OP, 16>(a, stages, occ, grid, st);
+}
+
+template <int KIND>
+hipError_t launch_lds(const CollArgs &a, int dt, int op, int stages, int occ, unsigned grid,
+                      hipStream_t st) {
+  if constexpr (KIND == KIND_AG) {
+    if (dt == CCL_BFLOAT16) return launch_lds_p<KIND, CCL_BFLOAT16, CCL_SUM>(a, stages, occ, grid, st);
+    return launch_lds_p<KIND, CCL_INT32, CCL_SUM>(a, stages, occ, grid, st);
+  } else {
+#define CCL_LO(D)                                                                        \
+  switch (op) {                                                                          \
+    case CCL_SUM: return launch_lds_p<KIND, D, CCL_SUM>(a, stages, occ, grid, st);       \
+    case CCL_MIN: return launch_lds_p<KIND, D, CCL_MIN>(a, stages, occ, grid, st);       \
+    default: return launch_lds_p<KIND, D, CCL_MAX>(a, stages, occ, grid, st);            \
+  }
+    switch (dt) {
+      case CCL_FLOAT32: CCL_LO(CCL_FLOAT32)
+      case CCL_BFLOAT16: CCL_LO(CCL_BFLOAT16)
+      default: CCL_LO(CCL_INT32)
+    }
+#undef CCL_LO
   }
 }
 
@@ -311,18 +583,25 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
   }
 
-  if (l.stages > 1) return CCL_ERR_UNSUPPORTED;  // LDS pipeline: not built yet
-
   a.chunk_vecs = l.chunk_bytes / kVecBytes;
   a.chunks_per_seg = std::max<uint64_t>(1, (max_nvec + a.chunk_vecs - 1) / a.chunk_vecs);
   a.total_chunks = a.chunks_per_seg * nseg;
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
   grid = std::min<uint64_t>(grid, a.total_chunks);
   grid = std::min<uint64_t>(grid, 1u << 30);
+  if (l.stages > 1) {
+    switch (d.kind) {
+      case KIND_AR: err = launch_lds<KIND_AR>(a, d.dtype, d.op, l.stages, l.occupancy, (unsigned)grid, stream); break;
+      case KIND_RS: err = launch_lds<KIND_RS>(a, d.dtype, d.op, l.stages, l.occupancy, (unsigned)grid, stream); break;
+      default: err = launch_lds<KIND_AG>(a, d.dtype, d.op, l.stages, l.occupancy, (unsigned)grid, stream); break;
+    }
+    return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+  }
+  const size_t lds = occupancy_lds(l.occupancy, 0);
   switch (d.kind) {
-    case KIND_AR: err = launch_dt<KIND_AR>(a, d.dtype, d.op, l.unroll, (unsigned)grid, stream); break;
-    case KIND_RS: err = launch_dt<KIND_RS>(a, d.dtype, d.op, l.unroll, (unsigned)grid, stream); break;
-    default: err = launch_dt<KIND_AG>(a, d.dtype, d.op, l.unroll, (unsigned)grid, stream); break;
+    case KIND_AR: err = launch_dt<KIND_AR>(a, d.dtype, d.op, l.unroll, (unsigned)grid, lds, stream); break;
+    case KIND_RS: err = launch_dt<KIND_RS>(a, d.dtype, d.op, l.unroll, (unsigned)grid, lds, stream); break;
+    default: err = launch_dt<KIND_AG>(a, d.dtype, d.op, l.unroll, (unsigned)grid, lds, stream); break;
   }
   return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

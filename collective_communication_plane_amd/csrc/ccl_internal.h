@@ -15,7 +15,20 @@ namespace ccl {
 constexpr int kVecBytes = 16;          // one dwordx4 per lane
 constexpr int kThreads = 256;          // register-direct workgroup: 4 wave64s
 constexpr int kLdsTileBytes = 4096;    // LDS pipeline: per-rank bytes per stage
-constexpr uint64_t kDefaultChunkBytes = 64 * 1024;
+// Launch defaults, picked by the launch sweep over chunk bytes, grid, unroll,
+// LDS stages and resident workgroups per CU on MI355X (P = 8, 256 MiB per
+// rank).  The common thread: capping residency at 2-3 workgroups per CU keeps
+// few DRAM pages open while 2P buffers stream at once.
+struct OpDefaults {
+  uint64_t chunk_bytes;
+  int stages;
+  int unroll;
+  int occupancy;
+};
+constexpr OpDefaults kDefaultsAR{4096, 1, 1, 3};
+constexpr OpDefaults kDefaultsRS{8192, 2, 2, 2};
+constexpr OpDefaults kDefaultsAG{4096, 2, 2, 2};
+constexpr OpDefaults kDefaultsReshard{16384, 1, 4, 2};
 
 inline int dtype_size(int dt) {
   switch (dt) {
@@ -36,7 +49,18 @@ struct Launch {
   int unroll;      // 1 or 2
   bool nt_load;
   bool nt_store;
+  int occupancy;   // max resident workgroups per CU, 0 = no cap
 };
+
+// Dynamic LDS to request so that at most `occupancy` workgroups fit on a CU
+// alongside `static_lds` bytes of their own; 0 when there is no cap.
+inline size_t occupancy_lds(int occupancy, size_t static_lds) {
+  constexpr size_t kLdsPerCu = 160 * 1024;
+  if (occupancy <= 0) return 0;
+  size_t per_wg = kLdsPerCu / (size_t)occupancy;
+  per_wg &= ~size_t(511);
+  return per_wg > static_lds ? per_wg - static_lds : 0;
+}
 
 // Collective launch description, all checks already passed.
 struct CollDesc {
@@ -52,7 +76,8 @@ struct CollDesc {
 // Compute units of a device (cached after the first query); <= 0 on error.
 int device_cu_count(int dev);
 
-ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Launch *out);
+enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3 };
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, Launch *out);
 ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t stream);
 
 // ------------------------------------------------------------------ reshard

@@ -178,7 +178,8 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   a.flags = (l.nt_load ? 1 : 0) | (l.nt_store ? 2 : 0);
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
-  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kThreads),
+                     occupancy_lds(l.occupancy, 0), stream, a);
   return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
 

@@ -66,23 +66,38 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
 
 /*
  * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
- * configuration is tuned by a sweep).  Pass NULL for the built-in defaults.
- * A zero field means "default"; out-of-range values give CCL_ERR_INVALID_ARG.
- * None of these fields changes any result.
+ * configuration is tuned by a sweep).  Pass NULL for the built-in defaults,
+ * which come from that sweep on MI355X (P = 8, 256 MiB per rank):
+ *   all-reduce      register-direct, 4 KiB chunks, unroll 1, <= 3 WGs per CU
+ *   reduce-scatter  LDS pipeline, 2 stages, 8 KiB chunks, <= 2 WGs per CU
+ *   all-gather      LDS pipeline, 2 stages, 4 KiB chunks, <= 2 WGs per CU
+ *   reshard copy    16 KiB chunks, <= 2 WGs per CU
+ * A zero field means "the default for this call"; out-of-range values give
+ * CCL_ERR_INVALID_ARG.  None of these fields changes any result.
  *
  *   chunk_bytes  contiguous bytes of each rank buffer one workgroup owns per
  *                scheduling step (its share of a shard); a multiple of 16,
- *                at least 1024 (for the LDS pipeline, a multiple of the
- *                pipeline's tile, 4096).
+ *                at least 1024.  The LDS pipeline needs a multiple of its
+ *                4096-byte tile: an explicit stages > 1 with another chunk
+ *                size is rejected, a default LDS choice falls back to
+ *                register-direct.
  *   workgroups   grid size; chunks are dealt to workgroups round-robin.
+ *                Default: one workgroup per chunk.
  *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS
  *                pipeline: producer waves stream tiles into a ring of
  *                `stages` LDS buffers with asynchronous global->LDS loads,
- *                consumer waves fold and store them.
+ *                consumer waves fold and store them (clamped so the ring
+ *                fits in 128 KiB).  The reshard copy is register-direct only.
  *   unroll       register-direct only: 16-byte vectors each lane keeps in
- *                flight per rank (1 or 2).
+ *                flight per rank (1, 2 or 4; 4 is used as 2 when P > 8).
  *   nontemporal  bit 0: nontemporal loads, bit 1: nontemporal stores;
  *                0 = default (both), 4 = neither.
+ *   occupancy    at most this many workgroups resident per compute unit
+ *                (enforced by reserving LDS), 1..32; 32 is effectively no
+ *                cap.  Fewer resident waves keep fewer DRAM pages open at
+ *                once, which is what lets P-stream kernels reach the HBM
+ *                bandwidth a single copy stream gets.
+ *   reserved     must be 0.
  */
 typedef struct {
     uint64_t chunk_bytes;
@@ -90,6 +105,8 @@ typedef struct {
     int32_t stages;
     int32_t unroll;
     int32_t nontemporal;
+    int32_t occupancy;
+    int32_t reserved;
 } ccl_launch_config_t;
 
 /*

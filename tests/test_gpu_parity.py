@@ -143,7 +143,7 @@ def test_bf16_rounding_ties_exercised():
 @pytest.mark.parametrize("cfg", [
     dict(chunk_bytes=1024), dict(chunk_bytes=16384), dict(chunk_bytes=1 << 20),
     dict(workgroups=1), dict(workgroups=7), dict(workgroups=1000),
-    dict(unroll=1), dict(unroll=2),
+    dict(unroll=1), dict(unroll=2), dict(unroll=4), dict(stages=2), dict(stages=4),
     dict(nontemporal=1), dict(nontemporal=2), dict(nontemporal=3), dict(nontemporal=4),
     dict(chunk_bytes=4096, workgroups=3, unroll=1, nontemporal=4),
 ])
@@ -296,3 +296,67 @@ def test_rejected_calls_touch_nothing():
     torch.cuda.synchronize()
     for b in dy:
         assert (b.base == b.fill).all().item()
+
+
+# --------------------------------------------------------- LDS pipeline
+
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("P", [1, 3, 8, 16])
+@pytest.mark.parametrize("chunk", [4096, 16384, 65536])
+def test_lds_pipeline_all_reduce(stages, P, chunk):
+    n = 5 * 8192 + 7  # several tiles and chunks plus a ragged tail
+    cfg = ccl.LaunchConfig(stages=stages, chunk_bytes=chunk)
+    for dtype, op in [("bf16", "sum"), ("f32", "max"), ("i32", "sum")]:
+        xs = si.rank_buffers(P, n, dtype, dist_of(dtype), seed=stages + P)
+        got = run_ar(xs, dtype, op, cfg=cfg)
+        want = oracle.all_reduce(xs, dtype, op)
+        for q in range(P):
+            assert_parity(got[q], want[q], dtype, op, f"LDS AR S={stages} P={P} {dtype}")
+
+
+@pytest.mark.parametrize("stages", [2, 4])
+@pytest.mark.parametrize("P", [2, 8, 16])
+def test_lds_pipeline_reduce_scatter_and_all_gather(stages, P):
+    cfg = ccl.LaunchConfig(stages=stages, chunk_bytes=8192)
+    m = 3 * 4096 + 5
+    xs = si.rank_buffers(P, P * m, "bf16", "uniform", seed=P)
+    got = run_rs(xs, "bf16", "sum", cfg=cfg)
+    want = oracle.reduce_scatter(xs, "bf16", "sum")
+    for s in range(P):
+        assert_parity(got[s], want[s], "bf16", "sum", f"LDS RS S={stages} P={P}")
+    xg = si.rank_buffers(P, m, "f32", "normal", seed=P + 1)
+    got = run_ag(xg, "f32", cfg=cfg)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
+
+
+@pytest.mark.parametrize("cfg", [dict(stages=2, workgroups=1), dict(stages=3, workgroups=5),
+                                 dict(stages=4, workgroups=300, nontemporal=4)])
+def test_lds_pipeline_few_workgroups_and_offsets(cfg):
+    P, n = 8, 70001
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=21)
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    for off in (0, 6):
+        got = run_ar(xs, "bf16", "sum", offset=off, cfg=ccl.LaunchConfig(chunk_bytes=16384, **cfg))
+        for q in range(P):
+            np.testing.assert_array_equal(got[q], want[q])
+
+
+@pytest.mark.parametrize("stages", [1, 2, 3])
+@pytest.mark.parametrize("P,m", [(1, 1), (2, 1), (3, 3), (4, 5), (8, 7), (16, 2)])
+def test_segments_without_whole_vectors(stages, P, m):
+    """Shards shorter than one 16-byte vector are all scalar head/tail."""
+    cfg = ccl.LaunchConfig(stages=stages, chunk_bytes=4096)
+    xs = si.rank_buffers(P, P * m, "f32", "uniform", seed=m)
+    got = run_rs(xs, "f32", "sum", cfg=cfg)
+    want = oracle.reduce_scatter(xs, "f32", "sum")
+    for s in range(P):
+        assert_parity(got[s], want[s], "f32", "sum", f"RS tiny S={stages}")
+    xb = si.rank_buffers(P, m, "bf16", "normal", seed=m)
+    got = run_ag(xb, "bf16", cfg=cfg)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xb))
+    got = run_ar(xb, "bf16", "max", cfg=cfg)
+    want = oracle.all_reduce(xb, "bf16", "max")
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want[q])
