@@ -27,6 +27,10 @@ Other modes:
   --calibrate   also runs a plain 1 GiB device copy (torch) a few times, the
                 known-size reference that scales rocprofv3's FETCH_SIZE and
                 WRITE_SIZE counters to bytes.
+  --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
+                16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
+                same kernel), with the default and an uncapped occupancy, next
+                to a plain 1 GiB device copy; one JSON line per point.
 """
 from __future__ import annotations
 
@@ -248,6 +252,38 @@ def sweep(dev, stream) -> None:
         print(json.dumps({"sweep_best": name, **best}), flush=True)
 
 
+def streams(dev, stream) -> None:
+    """All-reduce GB/s against P at a fixed total size (2 GiB in, 2 GiB out)."""
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = timed(lambda: dst.copy_(src), 20, 3, stream, 0.5)
+    print(json.dumps({"streams": "device_copy_1GiB", "ms": round(ms, 5),
+                      "GB/s": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    del src, dst
+    for P in (1, 2, 4, 8, 16):
+        n = (1 << 30) // P  # bf16 elements per rank: 2 GiB of input in total
+        dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
+        dy = [torch.empty_like(t) for t in dx]
+        for occ in (0, 32):
+            cfg = ccl.LaunchConfig(occupancy=occ) if occ else None
+            ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16,
+                                                            ccl.CCL_SUM, stream, cfg)),
+                       20, 3, stream, 0.2)
+            gbs = 2 * P * n * 2 / (ms * 1e-3) / 1e9
+            print(json.dumps({"streams": f"all_reduce_P{P}",
+                              "occupancy": occ or "default", "ms": round(ms, 5),
+                              "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}),
+                  flush=True)
+        del dx, dy
+        torch.cuda.empty_cache()
+
+
 def calibrate(dev) -> None:
     """A plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -270,6 +306,7 @@ def main() -> int:
     ap.add_argument("--row-steps", type=int, default=50)
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--streams", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -291,6 +328,9 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.sweep:
         sweep(dev, stream)
+        return 0
+    if args.streams:
+        streams(dev, stream)
         return 0
     if args.calibrate:
         calibrate(dev)

@@ -61,11 +61,8 @@ int device_cu_count(int dev) {
   return cached[dev];
 }
 
-ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, Launch *out) {
-  const OpDefaults &d = op == OP_AR   ? kDefaultsAR
-                        : op == OP_RS ? kDefaultsRS
-                        : op == OP_AG ? kDefaultsAG
-                                      : kDefaultsReshard;
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch *out) {
+  const OpDefaults d = default_launch(op, P);
   Launch l{d.chunk_bytes, 0, d.stages, d.unroll, true, true, d.occupancy};
   bool explicit_stages = false;
   if (cfg) {
@@ -125,7 +122,7 @@ int ccl_version(void) { return 100; }
 ccl_status_t ccl_all_reduce(const void *const *send, void *const *recv, int nranks, size_t count,
                             int dtype, int op, void *stream, const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AR, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AR, nranks, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
     return CCL_ERR_INVALID_ARG;
@@ -151,7 +148,7 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
                                 size_t recvcount, int dtype, int op, void *stream,
                                 const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RS, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RS, nranks, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op))
     return CCL_ERR_INVALID_ARG;
@@ -177,7 +174,7 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
                             size_t sendcount, int dtype, void *stream,
                             const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AG, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AG, nranks, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0) return CCL_ERR_INVALID_ARG;
   if (sendcount == 0) return CCL_OK;
@@ -202,7 +199,7 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
                               void *const *dst_bufs, void *stream,
                               const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD, 0, &l);
   if (st) return st;
   if (!plan || !src_bufs || !dst_bufs) return CCL_ERR_INVALID_ARG;
   ccl_plan *p = const_cast<ccl_plan *>(plan);

@@ -36,6 +36,9 @@ struct CollArgs {
   char *out[CCL_MAX_RANKS];
   uint64_t nvec[CCL_MAX_RANKS];   // 16-byte vectors in the body of segment s
   uint32_t head[CCL_MAX_RANKS];   // scalar elements before the body of segment s
+  // shift[s][r]: byte offset, mod 16, of input r's element at the start of
+  // segment s's vector body (the outputs are 16-byte aligned there).
+  uint8_t shift[CCL_MAX_RANKS][CCL_MAX_RANKS];
   uint64_t seg_elems;             // M
   uint64_t chunk_vecs;
   uint64_t chunks_per_seg;
@@ -166,7 +169,99 @@ __global__ void __launch_bounds__(kThreads) coll_vec_kernel(CollArgs a) {
   }
 }
 
-// Element-wise fallback for buffers that are not 16-byte aligned alike.
+// Realigning kernel: the outputs of each segment are 16-byte aligned at the
+// vector body, inputs may sit at any even byte offset from them.  An input at
+// offset d is read as the two aligned 16-byte blocks that cover its 16 bytes
+// and the wanted bytes are funnel-shifted out with v_alignbyte.  Both blocks
+// contain at least one byte of the input range, so neither leaves the pages
+// the input lives in.
+__device__ __forceinline__ uint32_t pick4(int q, uint32_t w0, uint32_t w1, uint32_t w2,
+                                          uint32_t w3) {
+  return q == 0 ? w0 : q == 1 ? w1 : q == 2 ? w2 : w3;
+}
+
+__device__ __forceinline__ u32x4 realign16(u32x4 A, u32x4 B, int d) {
+  const int q = d >> 2;
+  const unsigned r = (unsigned)(d & 3);
+  const uint32_t w[8] = {A[0], A[1], A[2], A[3], B[0], B[1], B[2], B[3]};
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t lo = pick4(q, w[j], w[j + 1], w[j + 2], w[j + 3]);
+    const uint32_t hi = pick4(q, w[j + 1], w[j + 2], w[j + 3], w[j + 4]);
+    o[j] = __builtin_amdgcn_alignbyte(hi, lo, r);
+  }
+  return o;
+}
+
+template <int KIND, int DT, int OP, int PMAX>
+__global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
+  constexpr int esz = DT == CCL_BFLOAT16 ? 2 : 4;
+  constexpr int V = kVecBytes / esz;
+  constexpr int NI = KIND == KIND_AG ? 1 : PMAX;
+  constexpr int NO = KIND == KIND_RS ? 1 : PMAX;
+  const int P = a.P;
+  const int ni = KIND == KIND_AG ? 1 : P;
+  const int no = KIND == KIND_RS ? 1 : P;
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
+
+  for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
+    const int s = (int)(c / a.chunks_per_seg);
+    const uint64_t lc = c - (uint64_t)s * a.chunks_per_seg;
+    const uint64_t nv = a.nvec[s];
+    const uint64_t head = a.head[s];
+    if (lc == 0) {
+      const uint64_t tail0 = head + nv * V;
+      const uint64_t ntail = a.seg_elems - tail0;
+      const uint64_t t = threadIdx.x;
+      if (t < head) scalar_element<KIND, DT, OP>(a, s, t);
+      else if (t - head < ntail) scalar_element<KIND, DT, OP>(a, s, tail0 + (t - head));
+    }
+    const uint64_t v0 = lc * a.chunk_vecs;
+    const uint64_t v1 = min(v0 + a.chunk_vecs, nv);
+    const char *ib[NI];
+    int sh[NI];
+    char *ob[NO];
+#pragma unroll
+    for (int r = 0; r < NI; ++r) {
+      sh[r] = r < ni ? a.shift[s][r] : 0;
+      ib[r] = r < ni ? in_at<KIND>(a, s, r, head, esz) - sh[r] : nullptr;  // aligned block
+    }
+#pragma unroll
+    for (int q = 0; q < NO; ++q) ob[q] = q < no ? out_at<KIND>(a, s, q, head, esz) : nullptr;
+
+    for (uint64_t v = v0 + threadIdx.x; v < v1; v += kThreads) {
+      u32x4 x[NI];
+#pragma unroll
+      for (int r = 0; r < NI; ++r) {
+        if (r < ni) {
+          const char *p = ib[r] + v * kVecBytes;
+          const u32x4 A = ntl ? ld_nt(p) : ld_plain(p);
+          if (sh[r]) {
+            const u32x4 B = ntl ? ld_nt(p + kVecBytes) : ld_plain(p + kVecBytes);
+            x[r] = realign16(A, B, sh[r]);
+          } else {
+            x[r] = A;
+          }
+        }
+      }
+      u32x4 y;
+      if constexpr (KIND == KIND_AG) y = x[0];
+      else y = fold_vec<DT, OP, NI>(x, ni);
+      if (nts) {
+#pragma unroll
+        for (int q = 0; q < NO; ++q)
+          if (q < no) st_nt(ob[q] + v * kVecBytes, y);
+      } else {
+#pragma unroll
+        for (int q = 0; q < NO; ++q)
+          if (q < no) st_plain(ob[q] + v * kVecBytes, y);
+      }
+    }
+  }
+}
+
+// Element-wise fallback for outputs that are not 16-byte aligned alike.
 template <int KIND, int DT, int OP>
 __global__ void __launch_bounds__(kThreads) coll_scalar_kernel(CollArgs a, int nseg) {
   const uint64_t total = (uint64_t)nseg * a.seg_elems;
@@ -492,6 +587,39 @@ hipError_t launch_lds(const CollArgs &a, int dt, int op, int stages, int occ, un
 }
 
 template <int KIND, int DT, int OP>
+hipError_t launch_realign_p(const CollArgs &a, unsigned grid, size_t lds, hipStream_t st) {
+  if (a.P <= 4)
+    hipLaunchKernelGGL((coll_realign_kernel<KIND, DT, OP, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (a.P <= 8)
+    hipLaunchKernelGGL((coll_realign_kernel<KIND, DT, OP, 8>), dim3(grid), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((coll_realign_kernel<KIND, DT, OP, 16>), dim3(grid), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_realign(const CollArgs &a, int dt, int op, unsigned grid, size_t lds,
+                          hipStream_t st) {
+  if constexpr (KIND == KIND_AG) {
+    if (dt == CCL_BFLOAT16) return launch_realign_p<KIND, CCL_BFLOAT16, CCL_SUM>(a, grid, lds, st);
+    return launch_realign_p<KIND, CCL_INT32, CCL_SUM>(a, grid, lds, st);
+  } else {
+#define CCL_RA(D)                                                                 \
+  switch (op) {                                                                   \
+    case CCL_SUM: return launch_realign_p<KIND, D, CCL_SUM>(a, grid, lds, st);    \
+    case CCL_MIN: return launch_realign_p<KIND, D, CCL_MIN>(a, grid, lds, st);    \
+    default: return launch_realign_p<KIND, D, CCL_MAX>(a, grid, lds, st);         \
+  }
+    switch (dt) {
+      case CCL_FLOAT32: CCL_RA(CCL_FLOAT32)
+      case CCL_BFLOAT16: CCL_RA(CCL_BFLOAT16)
+      default: CCL_RA(CCL_INT32)
+    }
+#undef CCL_RA
+  }
+}
+
+template <int KIND, int DT, int OP>
 hipError_t launch_scalar3(const CollArgs &a, int nseg, unsigned grid, hipStream_t st) {
   hipLaunchKernelGGL((coll_scalar_kernel<KIND, DT, OP>), dim3(grid), dim3(kThreads), 0, st, a, nseg);
   return hipGetLastError();
@@ -536,33 +664,34 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   const int ni = d.kind == KIND_AG ? 1 : d.P;
   const int no = d.kind == KIND_RS ? 1 : d.P;
 
-  // Every buffer of a segment must share its address modulo 16 for the
-  // vector path; the common misalignment becomes the scalar head.
-  bool vec = true;
+  // The outputs of a segment must share their address modulo 16; their
+  // common misalignment becomes the scalar head, after which every output is
+  // 16-byte aligned.  Inputs at another offset are realigned in registers.
+  bool vec = true, realign = false;
   uint64_t max_nvec = 0;
   for (int s = 0; s < nseg && vec; ++s) {
-    uintptr_t base[2 * CCL_MAX_RANKS];
-    int nb = 0;
-    for (int r = 0; r < ni; ++r) {
-      const char *p = d.kind == KIND_AR ? a.in[r]
-                      : d.kind == KIND_RS ? a.in[r] + (uint64_t)s * M * esz
-                                          : a.in[s];
-      base[nb++] = (uintptr_t)p;
-    }
+    uintptr_t ob[CCL_MAX_RANKS];
     for (int q = 0; q < no; ++q) {
       const char *p = d.kind == KIND_AR ? a.out[q]
                       : d.kind == KIND_RS ? a.out[s]
                                           : a.out[q] + (uint64_t)s * M * esz;
-      base[nb++] = (uintptr_t)p;
+      ob[q] = (uintptr_t)p;
     }
-    const uintptr_t mis = base[0] % kVecBytes;
-    for (int i = 1; i < nb; ++i)
-      if (base[i] % kVecBytes != mis) vec = false;
+    const uintptr_t mis = ob[0] % kVecBytes;
+    for (int q = 1; q < no; ++q)
+      if (ob[q] % kVecBytes != mis) vec = false;
     uint64_t head = ((kVecBytes - mis) % kVecBytes) / esz;
     if (head > M) head = M;
     a.head[s] = (uint32_t)head;
     a.nvec[s] = (M - head) / V;
     max_nvec = std::max<uint64_t>(max_nvec, a.nvec[s]);
+    for (int r = 0; r < ni; ++r) {
+      const char *p = d.kind == KIND_AR ? a.in[r]
+                      : d.kind == KIND_RS ? a.in[r] + (uint64_t)s * M * esz
+                                          : a.in[s];
+      a.shift[s][r] = (uint8_t)(((uintptr_t)p + head * esz) % kVecBytes);
+      if (a.shift[s][r]) realign = true;
+    }
   }
 
   int dev = 0;
@@ -589,6 +718,15 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
   grid = std::min<uint64_t>(grid, a.total_chunks);
   grid = std::min<uint64_t>(grid, 1u << 30);
+  if (realign) {
+    const size_t lds = occupancy_lds(l.occupancy, 0);
+    switch (d.kind) {
+      case KIND_AR: err = launch_realign<KIND_AR>(a, d.dtype, d.op, (unsigned)grid, lds, stream); break;
+      case KIND_RS: err = launch_realign<KIND_RS>(a, d.dtype, d.op, (unsigned)grid, lds, stream); break;
+      default: err = launch_realign<KIND_AG>(a, d.dtype, d.op, (unsigned)grid, lds, stream); break;
+    }
+    return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+  }
   if (l.stages > 1) {
     switch (d.kind) {
       case KIND_AR: err = launch_lds<KIND_AR>(a, d.dtype, d.op, l.stages, l.occupancy, (unsigned)grid, stream); break;

@@ -15,20 +15,37 @@ namespace ccl {
 constexpr int kVecBytes = 16;          // one dwordx4 per lane
 constexpr int kThreads = 256;          // register-direct workgroup: 4 wave64s
 constexpr int kLdsTileBytes = 4096;    // LDS pipeline: per-rank bytes per stage
-// Launch defaults, picked by the launch sweep over chunk bytes, grid, unroll,
-// LDS stages and resident workgroups per CU on MI355X (P = 8, 256 MiB per
-// rank).  The common thread: capping residency at 2-3 workgroups per CU keeps
-// few DRAM pages open while 2P buffers stream at once.
+// Launch defaults, from the launch sweep over chunk bytes, unroll, LDS stages
+// and resident workgroups per CU on MI355X (2 GiB of input spread over P
+// ranks, bf16).  The common thread: with 2P buffers streaming at once, capping
+// residency keeps few DRAM pages open; with few buffers each workgroup has
+// little in flight, so the cap is looser.
 struct OpDefaults {
   uint64_t chunk_bytes;
   int stages;
   int unroll;
   int occupancy;
 };
-constexpr OpDefaults kDefaultsAR{4096, 1, 1, 3};
-constexpr OpDefaults kDefaultsRS{8192, 2, 2, 2};
-constexpr OpDefaults kDefaultsAG{4096, 2, 2, 2};
-constexpr OpDefaults kDefaultsReshard{16384, 1, 4, 2};
+
+enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3 };
+
+inline OpDefaults default_launch(Op op, int P) {
+  switch (op) {
+    case OP_AR:
+      return P <= 2 ? OpDefaults{8192, 1, 2, 8} : OpDefaults{4096, 1, 1, 3};
+    case OP_RS:
+      if (P <= 2) return {8192, 1, 2, 4};
+      if (P >= 7 && P <= 12) return {8192, 2, 2, 2};
+      return {8192, 1, 2, 3};
+    case OP_AG:
+      if (P <= 2) return {8192, 1, 2, 4};
+      if (P >= 7 && P <= 12) return {4096, 2, 2, 3};
+      if (P >= 13) return {8192, 1, 2, 1};
+      return {8192, 1, 2, 3};
+    default:
+      return {16384, 1, 4, 2};
+  }
+}
 
 inline int dtype_size(int dt) {
   switch (dt) {
@@ -76,8 +93,7 @@ struct CollDesc {
 // Compute units of a device (cached after the first query); <= 0 on error.
 int device_cu_count(int dev);
 
-enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3 };
-ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, Launch *out);
+ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch *out);
 ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t stream);
 
 // ------------------------------------------------------------------ reshard
@@ -93,7 +109,9 @@ struct PlanInterval {
 
 struct DevicePlanCache {
   int device = -1;
-  void *table = nullptr;  // device copy of the interval + replica tables
+  void *table = nullptr;  // device copy of the interval, replica and chunk tables
+  size_t rep_offset = 0;       // byte offset of the replica table
+  size_t chunk_iv_offset = 0;  // byte offset of the chunk -> interval table (0: none)
   uint64_t chunk_bytes = 0;
   uint64_t total_chunks = 0;
 };
@@ -109,6 +127,7 @@ struct ccl_plan {
   std::vector<uint64_t> dst_local_bytes;  // per destination-mesh rank
   std::vector<std::vector<int32_t>> replicas;  // per dst shard: local dst indices, ascending
   std::vector<ccl::PlanInterval> intervals;
+  bool offsets_aligned16 = true;         // every interval offset is a multiple of 16
   // Device-side state, created on first use.
   std::mutex mu;
   std::vector<ccl::DevicePlanCache> dev;

@@ -199,6 +199,8 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
         p->intervals[j].leader = D.start + rep[(j - first) % rep.size()];
     }
   }
+  for (const auto &iv : p->intervals)
+    if (iv.src_off % 16 || iv.dst_off % 16) p->offsets_aligned16 = false;
   *plan_out = p;
   return CCL_OK;
 }

@@ -9,10 +9,12 @@
 // so a shard with rho replicas costs 1 read + rho writes instead of the
 // 1 + 1 + 2(rho - 1) of a leader-then-copy scheme.
 //
-// Work decomposition: every interval is cut into chunks of chunk_bytes;
-// chunk c of the plan belongs to the interval whose first chunk index is the
-// largest one <= c (binary search over a prefix table).  Chunks are dealt to
-// workgroups round-robin.
+// Work decomposition: every interval is cut into chunks of chunk_bytes and
+// chunks are dealt to workgroups round-robin.  A per-chunk table maps chunk c
+// to its interval (plans with more than 2^24 chunks fall back to a binary
+// search over the intervals' first-chunk indices).  When every buffer base
+// and every interval offset is 16-byte aligned (checked on the host) the
+// kernel skips its per-chunk alignment test.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -25,6 +27,7 @@ namespace ccl {
 namespace {
 
 constexpr int kReshardUnroll = 4;
+constexpr uint64_t kMaxChunkTable = uint64_t(1) << 24;
 
 struct DevInterval {
   uint64_t src_off;
@@ -39,12 +42,14 @@ struct ReshardArgs {
   const char *src[CCL_MAX_MESH_RANKS];
   char *dst[CCL_MAX_MESH_RANKS];
   const DevInterval *iv;
-  const int32_t *rep;  // rep[shard * rho + j] = local index of replica j
+  const int32_t *rep;       // rep[shard * rho + j] = local index of replica j
+  const uint32_t *chunk_iv; // interval of each chunk, or null (binary search)
   uint64_t total_chunks;
   uint64_t chunk_bytes;
   int n_iv;
   int rho;
   int flags;           // bit 0: nontemporal loads, bit 1: nontemporal stores
+  int aligned;         // every base and interval offset is 16-byte aligned
 };
 
 __device__ __forceinline__ int find_interval(const DevInterval *iv, int n, uint64_t c) {
@@ -60,7 +65,7 @@ __device__ __forceinline__ int find_interval(const DevInterval *iv, int n, uint6
 __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
   const bool ntl = a.flags & 1, nts = a.flags & 2;
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
-    const int i = find_interval(a.iv, a.n_iv, c);
+    const int i = a.chunk_iv ? (int)a.chunk_iv[c] : find_interval(a.iv, a.n_iv, c);
     const DevInterval iv = a.iv[i];
     const uint64_t off = (c - iv.first_chunk) * a.chunk_bytes;
     const uint64_t bytes = min(a.chunk_bytes, iv.len - off);
@@ -71,8 +76,9 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
     // Vector path when every address shares the source's alignment mod 16.
     const uintptr_t mis = (uintptr_t)src % kVecBytes;
     bool same = true;
-    for (int j = 0; j < a.rho; ++j)
-      same &= ((uintptr_t)(a.dst[rep[j]] + dst_base) % kVecBytes) == mis;
+    if (!a.aligned)
+      for (int j = 0; j < a.rho; ++j)
+        same &= ((uintptr_t)(a.dst[rep[j]] + dst_base) % kVecBytes) == mis;
     if (!same) {
       for (uint64_t b = threadIdx.x; b < bytes; b += kThreads) {
         const char v = src[b];
@@ -134,20 +140,33 @@ ccl_status_t device_table(ccl_plan *p, int dev, uint64_t chunk_bytes, DevicePlan
   std::vector<int32_t> rep((size_t)p->n_dst_shards * rho);
   for (int t = 0; t < p->n_dst_shards; ++t)
     for (int j = 0; j < rho; ++j) rep[(size_t)t * rho + j] = p->replicas[t][j];
+  std::vector<uint32_t> civ;
+  if (chunk <= kMaxChunkTable) {
+    civ.resize(chunk);
+    for (size_t i = 0; i < n; ++i) {
+      const uint64_t end = i + 1 < n ? host[i + 1].first_chunk : chunk;
+      for (uint64_t c = host[i].first_chunk; c < end; ++c) civ[c] = (uint32_t)i;
+    }
+  }
   const size_t iv_bytes = n * sizeof(DevInterval);
-  const size_t bytes = iv_bytes + rep.size() * sizeof(int32_t);
+  const size_t rep_bytes = (rep.size() * sizeof(int32_t) + 15) & ~size_t(15);
+  const size_t bytes = iv_bytes + rep_bytes + civ.size() * sizeof(uint32_t);
   void *mem = nullptr;
   if (hipMalloc(&mem, bytes) != hipSuccess) return CCL_ERR_NOMEM;
   // Synchronous copies: the host staging vectors die when this returns.
   if (hipMemcpy(mem, host.data(), iv_bytes, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy((char *)mem + iv_bytes, rep.data(), rep.size() * sizeof(int32_t),
-                hipMemcpyHostToDevice) != hipSuccess) {
+                hipMemcpyHostToDevice) != hipSuccess ||
+      (!civ.empty() && hipMemcpy((char *)mem + iv_bytes + rep_bytes, civ.data(),
+                                 civ.size() * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)) {
     (void)hipFree(mem);
     return CCL_ERR_HIP;
   }
   DevicePlanCache e;
   e.device = dev;
   e.table = mem;
+  e.rep_offset = iv_bytes;
+  e.chunk_iv_offset = civ.empty() ? 0 : iv_bytes + rep_bytes;
   e.chunk_bytes = chunk_bytes;
   e.total_chunks = chunk;
   p->dev.push_back(e);
@@ -170,7 +189,13 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   for (int i = 0; i < p->n_src; ++i) a.src[i] = (const char *)src[i];
   for (int i = 0; i < p->n_dst; ++i) a.dst[i] = (char *)dst[i];
   a.iv = (const DevInterval *)e.table;
-  a.rep = (const int32_t *)((const char *)e.table + p->intervals.size() * sizeof(DevInterval));
+  a.rep = (const int32_t *)((const char *)e.table + e.rep_offset);
+  a.chunk_iv = e.chunk_iv_offset ? (const uint32_t *)((const char *)e.table + e.chunk_iv_offset)
+                                  : nullptr;
+  bool aligned = p->offsets_aligned16;
+  for (int i = 0; i < p->n_src && aligned; ++i) aligned = (uintptr_t)src[i] % kVecBytes == 0;
+  for (int i = 0; i < p->n_dst && aligned; ++i) aligned = (uintptr_t)dst[i] % kVecBytes == 0;
+  a.aligned = aligned && l.chunk_bytes % kVecBytes == 0;
   a.total_chunks = e.total_chunks;
   a.chunk_bytes = l.chunk_bytes;
   a.n_iv = (int)p->intervals.size();

@@ -67,11 +67,18 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
 /*
  * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
  * configuration is tuned by a sweep).  Pass NULL for the built-in defaults,
- * which come from that sweep on MI355X (P = 8, 256 MiB per rank):
- *   all-reduce      register-direct, 4 KiB chunks, unroll 1, <= 3 WGs per CU
- *   reduce-scatter  LDS pipeline, 2 stages, 8 KiB chunks, <= 2 WGs per CU
- *   all-gather      LDS pipeline, 2 stages, 4 KiB chunks, <= 2 WGs per CU
+ * which come from that sweep on MI355X (2 GiB of bf16 input over P ranks):
+ *   all-reduce      P <= 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
+ *                   P >= 3: 4 KiB chunks, unroll 1, <= 3 WGs per CU
+ *   reduce-scatter  7 <= P <= 12: LDS pipeline, 2 stages, 8 KiB chunks,
+ *                   <= 2 WGs per CU; otherwise register-direct, 8 KiB chunks,
+ *                   unroll 2, <= 4 (P <= 2) or 3 WGs per CU
+ *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
+ *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
+ *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
  *   reshard copy    16 KiB chunks, <= 2 WGs per CU
+ * Buffers whose inputs sit at a different offset mod 16 from their outputs
+ * use a register-direct kernel that realigns the inputs in VGPRs.
  * A zero field means "the default for this call"; out-of-range values give
  * CCL_ERR_INVALID_ARG.  None of these fields changes any result.
  *

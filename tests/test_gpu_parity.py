@@ -92,7 +92,7 @@ def test_all_reduce_unaligned_alike(offset, dtype):
 
 
 def test_all_reduce_misaligned_relative_to_each_other():
-    """Inputs at offset 0, outputs at offset 4: the element-wise kernel runs."""
+    """Inputs at offset 0, outputs at offset 4: inputs are realigned in VGPRs."""
     xs = si.rank_buffers(4, 5003, "f32", "uniform", seed=3)
     got = run_ar(xs, "f32", "max", offset=0, out_offset=4)
     want = oracle.all_reduce(xs, "f32", "max")
@@ -360,3 +360,98 @@ def test_segments_without_whole_vectors(stages, P, m):
     want = oracle.all_reduce(xb, "bf16", "max")
     for q in range(P):
         np.testing.assert_array_equal(got[q], want[q])
+
+
+# ------------------------------------------------- realigned and element-wise paths
+
+def run_offsets(kind, xs, dtype, op, in_offs, out_offs, cfg=None):
+    """Run one collective with a separate byte offset per input and output buffer."""
+    P = len(xs)
+    e = ESZ[dtype]
+    if kind == "ar":
+        n_in, n_out, cnt = xs[0].size, xs[0].size, xs[0].size
+    elif kind == "rs":
+        n_in, n_out, cnt = xs[0].size, xs[0].size // P, xs[0].size // P
+    else:
+        n_in, n_out, cnt = xs[0].size, P * xs[0].size, xs[0].size
+    dx = [DevBuf(n_in * e, DEV, o).upload(x) for x, o in zip(xs, in_offs)]
+    dy = [DevBuf(n_out * e, DEV, o) for o in out_offs]
+    fn = {"ar": lambda: ccl.ccl_all_reduce([b.ptr for b in dx], [b.ptr for b in dy], P, cnt,
+                                           ccl.DTYPES[dtype], ccl.OPS[op], stream(), cfg),
+          "rs": lambda: ccl.ccl_reduce_scatter([b.ptr for b in dx], [b.ptr for b in dy], P, cnt,
+                                               ccl.DTYPES[dtype], ccl.OPS[op], stream(), cfg),
+          "ag": lambda: ccl.ccl_all_gather([b.ptr for b in dx], [b.ptr for b in dy], P, cnt,
+                                           ccl.DTYPES[dtype], stream(), cfg)}[kind]
+    ccl.check(fn(), kind)
+    torch.cuda.synchronize()
+    for b in dx + dy:
+        assert b.guards_intact()
+    return [b.download(NP[dtype]) for b in dy]
+
+
+@pytest.mark.parametrize("P", [2, 3, 5, 8])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("m", [4097, 12289 * 3 + 1])
+def test_ragged_shards_take_the_realigned_path(P, dtype, m):
+    """Shard sizes that are not a multiple of 16 bytes put each segment's inputs
+    and outputs at different offsets mod 16."""
+    xs = si.rank_buffers(P, P * m, dtype, "uniform", seed=P + m)
+    got = run_offsets("rs", xs, dtype, "sum", [0] * P, [0] * P)
+    want = oracle.reduce_scatter(xs, dtype, "sum")
+    for s_ in range(P):
+        assert_parity(got[s_], want[s_], dtype, "sum", f"RS ragged P={P} m={m}")
+    xg = si.rank_buffers(P, m, dtype, "normal", seed=m)
+    got = run_offsets("ag", xg, dtype, "sum", [0] * P, [0] * P)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "i32"])
+def test_inputs_at_assorted_offsets(dtype):
+    """Every input at its own offset; outputs aligned alike (realigned path)."""
+    P, n = 6, 30011
+    step = ESZ[dtype]
+    offs = [(k * step * 3) % 16 for k in range(P)]
+    xs = si.rank_buffers(P, n, dtype, dist_of(dtype), seed=31)
+    for op in ("sum", "max"):
+        got = run_offsets("ar", xs, dtype, op, offs, [4 % 16 if step == 4 else 2] * P)
+        want = oracle.all_reduce(xs, dtype, op)
+        for q in range(P):
+            assert_parity(got[q], want[q], dtype, op, f"AR assorted offsets {op}")
+
+
+def test_outputs_misaligned_to_each_other_use_elementwise_kernel():
+    P, n = 4, 20003
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=41)
+    outs = [0, 2, 4, 6]
+    got = run_offsets("ar", xs, "bf16", "sum", [0] * P, outs)
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    for q in range(P):
+        assert_parity(got[q], want[q], "bf16", "sum", "AR outputs misaligned")
+    xr = si.rank_buffers(P, P * 1001, "f32", "uniform", seed=42)
+    got = run_offsets("rs", xr, "f32", "min", [0, 4, 8, 12], [4, 0, 12, 8])
+    want = oracle.reduce_scatter(xr, "f32", "min")
+    for s_ in range(P):
+        np.testing.assert_array_equal(got[s_], want[s_])
+    xg = si.rank_buffers(P, 777, "bf16", "normal", seed=43)
+    got = run_offsets("ag", xg, "bf16", "sum", [2, 0, 6, 4], [0, 2, 4, 8])
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 6, 8, 12, 16])
+def test_default_launch_for_every_rank_count(P):
+    """The defaults change with P (LDS pipeline for 7..12 ranks, different caps)."""
+    m = 3 * 4096 + 8
+    xs = si.rank_buffers(P, P * m, "bf16", "uniform", seed=P)
+    got = run_rs(xs, "bf16", "sum")
+    want = oracle.reduce_scatter(xs, "bf16", "sum")
+    for s_ in range(P):
+        assert_parity(got[s_], want[s_], "bf16", "sum", f"RS default P={P}")
+    got = run_ag(xs[:P], "bf16")
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xs))
+    got = run_ar(xs, "bf16", "sum")
+    want = oracle.all_reduce(xs, "bf16", "sum")
+    for q in range(P):
+        assert_parity(got[q], want[q], "bf16", "sum", f"AR default P={P}")
