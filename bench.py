@@ -47,7 +47,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (and % of roofline) for all_reduce P=8, 256 MB bf16"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "all_reduce_p8_256MiB_bf16_traffic.txt")
-KERNEL_SOURCES = ["ccl_collectives.hip", "ccl_device.h"]
+KERNEL_SOURCES = ["ccl_coll_kernels.h", "ccl_coll_inst.hip", "ccl_device.h"]
 
 
 def kernel_source_hash() -> str:

@@ -29,6 +29,7 @@ CCL_ERR_NOMEM = 6
 CCL_FLOAT32 = 0
 CCL_BFLOAT16 = 1
 CCL_INT32 = 2
+CCL_FLOAT16 = 3
 
 CCL_SUM = 0
 CCL_MIN = 1
@@ -42,7 +43,7 @@ CCL_MAX_MESH_DIMS = 4
 CCL_MAX_TENSOR_DIMS = 8
 CCL_MAX_MESH_RANKS = 64
 
-DTYPES = {"f32": CCL_FLOAT32, "bf16": CCL_BFLOAT16, "i32": CCL_INT32}
+DTYPES = {"f32": CCL_FLOAT32, "bf16": CCL_BFLOAT16, "i32": CCL_INT32, "f16": CCL_FLOAT16}
 OPS = {"sum": CCL_SUM, "min": CCL_MIN, "max": CCL_MAX}
 
 
@@ -83,7 +84,8 @@ class CclError(RuntimeError):
 _lib = None
 
 EXPORTS = [
-    "ccl_all_reduce", "ccl_reduce_scatter", "ccl_all_gather", "ccl_reshard_plan",
+    "ccl_all_reduce", "ccl_reduce_scatter", "ccl_all_gather", "ccl_reduce", "ccl_broadcast",
+    "ccl_reshard_plan",
     "ccl_reshard_copy", "ccl_plan_destroy", "ccl_plan_num_intervals", "ccl_plan_get_interval",
     "ccl_plan_local_bytes", "ccl_plan_num_dst_shards", "ccl_plan_shard_replicas",
     "ccl_get_error_string", "ccl_version",
@@ -109,6 +111,8 @@ def _load():
     lib.ccl_all_reduce.argtypes = [pp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_reduce_scatter.argtypes = [pp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_all_gather.argtypes = [pp, pp, i32, sz, i32, vp, pcfg]
+    lib.ccl_reduce.argtypes = [pp, vp, i32, sz, i32, i32, i32, vp, pcfg]
+    lib.ccl_broadcast.argtypes = [vp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_reshard_plan.argtypes = [ctypes.POINTER(TensorDesc), ctypes.POINTER(Mesh),
                                      ctypes.POINTER(Placement), ctypes.POINTER(Mesh),
                                      ctypes.POINTER(Placement), ctypes.POINTER(vp)]
@@ -188,6 +192,20 @@ def ccl_all_gather(send, recv, nranks: int, sendcount: int, dtype: int, stream=N
     s, r = _ptr_array(send), _ptr_array(recv)
     return _load().ccl_all_gather(_pp(s), _pp(r), nranks, sendcount, dtype, _stream(stream),
                                   _cfg(cfg))
+
+
+def ccl_reduce(send, recv, nranks: int, count: int, dtype: int, op: int, root: int = 0,
+               stream=None, cfg=None) -> int:
+    s = _ptr_array(send)
+    return _load().ccl_reduce(_pp(s), _addr(recv), nranks, count, dtype, op, root,
+                              _stream(stream), _cfg(cfg))
+
+
+def ccl_broadcast(send, recv, nranks: int, count: int, dtype: int, root: int = 0, stream=None,
+                  cfg=None) -> int:
+    r = _ptr_array(recv)
+    return _load().ccl_broadcast(_addr(send), _pp(r), nranks, count, dtype, root,
+                                 _stream(stream), _cfg(cfg))
 
 
 def make_mesh(dims: Sequence[int], start_rank: int) -> Mesh:

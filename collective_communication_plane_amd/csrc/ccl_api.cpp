@@ -140,7 +140,7 @@ ccl_status_t ccl_all_reduce(const void *const *send, void *const *recv, int nran
       Range x{(uintptr_t)send[r], (uintptr_t)send[r] + bytes};
       if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
     }
-  ccl::CollDesc d{ccl::KIND_AR, nranks, dtype, op, count, send, recv};
+  ccl::CollDesc d{ccl::KIND_AR, nranks, dtype, op, count, send, recv, false};
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
 
@@ -166,7 +166,7 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
       Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
       if (overlap(x, y) && y.lo != x.lo + (uint64_t)s * out_bytes) return CCL_ERR_ALIASING;
     }
-  ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, recvcount, send, recv};
+  ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, recvcount, send, recv, false};
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
 
@@ -191,7 +191,58 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
       Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
       if (overlap(x, y) && x.lo != y.lo + (uint64_t)r * in_bytes) return CCL_ERR_ALIASING;
     }
-  ccl::CollDesc d{ccl::KIND_AG, nranks, dtype, CCL_SUM, sendcount, send, recv};
+  ccl::CollDesc d{ccl::KIND_AG, nranks, dtype, CCL_SUM, sendcount, send, recv, false};
+  return ccl::launch_collective(d, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t count, int dtype,
+                        int op, int root, void *stream, const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RS, nranks, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || !op_ok(op) || root < 0 ||
+      root >= nranks)
+    return CCL_ERR_INVALID_ARG;
+  if (count == 0) return CCL_OK;
+  void *const recv1[1] = {recv};
+  if (!send || !recv || (uintptr_t)recv % (uintptr_t)dtype_size(dtype)) return CCL_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r)
+    if (!send[r] || (uintptr_t)send[r] % (uintptr_t)dtype_size(dtype)) return CCL_ERR_INVALID_ARG;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(count, sz)) return CCL_ERR_INVALID_ARG;
+  const uint64_t bytes = count * sz;
+  for (int r = 0; r < nranks; ++r) {
+    Range y{(uintptr_t)recv, (uintptr_t)recv + bytes};
+    Range x{(uintptr_t)send[r], (uintptr_t)send[r] + bytes};
+    if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
+  }
+  ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, count, send, recv1, true};
+  return ccl::launch_collective(d, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_broadcast(const void *send, void *const *recv, int nranks, size_t count,
+                           int dtype, int root, void *stream, const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AG, nranks, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS || dtype_size(dtype) == 0 || root < 0 ||
+      root >= nranks)
+    return CCL_ERR_INVALID_ARG;
+  if (count == 0) return CCL_OK;
+  const void *const send1[1] = {send};
+  if (!send || !recv || (uintptr_t)send % (uintptr_t)dtype_size(dtype)) return CCL_ERR_INVALID_ARG;
+  for (int q = 0; q < nranks; ++q)
+    if (!recv[q] || (uintptr_t)recv[q] % (uintptr_t)dtype_size(dtype)) return CCL_ERR_INVALID_ARG;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(count, sz)) return CCL_ERR_INVALID_ARG;
+  const uint64_t bytes = count * sz;
+  if ((st = check_outputs_disjoint(recv, nranks, bytes))) return st;
+  for (int q = 0; q < nranks; ++q) {
+    Range y{(uintptr_t)recv[q], (uintptr_t)recv[q] + bytes};
+    Range x{(uintptr_t)send, (uintptr_t)send + bytes};
+    if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
+  }
+  ccl::CollDesc d{ccl::KIND_AG, nranks, dtype, CCL_SUM, count, send1, recv, true};
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
 

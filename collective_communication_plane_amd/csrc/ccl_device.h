@@ -32,6 +32,18 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
   return ((u & 0x7fffffffu) > 0x7f800000u) ? 0x7fc0u : r;
 }
 
+// fp16 <-> fp32: widening is exact; narrowing rounds to nearest even (the
+// default rounding mode), fp16 denormals kept.
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ uint32_t f16_rne(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // One fold step.  min/max are compare-and-select so a tie (including +0 vs
 // -0) keeps the accumulated (earlier-rank) value.
 template <int OP>
@@ -52,7 +64,26 @@ __device__ __forceinline__ int32_t fold_i32(int32_t acc, int32_t v) {
 template <int DT, int OP, int NI>
 __device__ __forceinline__ u32x4 fold_vec(const u32x4 (&x)[NI], int n) {
   u32x4 y;
-  if constexpr (DT == CCL_BFLOAT16) {
+  if constexpr (DT == CCL_FLOAT16) {
+    float a[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[2 * k] = f16_lo(x[0][k]);
+      a[2 * k + 1] = f16_hi(x[0][k]);
+    }
+#pragma unroll
+    for (int r = 1; r < NI; ++r) {
+      if (r < n) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          a[2 * k] = fold_f32<OP>(a[2 * k], f16_lo(x[r][k]));
+          a[2 * k + 1] = fold_f32<OP>(a[2 * k + 1], f16_hi(x[r][k]));
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = f16_rne(a[2 * k]) | (f16_rne(a[2 * k + 1]) << 16);
+  } else if constexpr (DT == CCL_BFLOAT16) {
     float a[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {

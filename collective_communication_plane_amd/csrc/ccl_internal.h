@@ -52,6 +52,7 @@ inline int dtype_size(int dt) {
     case CCL_FLOAT32: return 4;
     case CCL_BFLOAT16: return 2;
     case CCL_INT32: return 4;
+    case CCL_FLOAT16: return 2;
     default: return 0;
   }
 }
@@ -88,6 +89,7 @@ struct CollDesc {
   uint64_t seg_elems;  // AR: count, RS: recvcount, AG: sendcount
   const void *const *send;
   void *const *recv;
+  bool single;         // one segment: reduce (KIND_RS) or broadcast (KIND_AG)
 };
 
 // Compute units of a device (cached after the first query); <= 0 on error.

@@ -26,9 +26,9 @@
  *     kernel surface at the caller's next synchronization.
  *   - A count of 0 is a valid no-op (pointers are then not inspected).
  *   - Reductions are computed per element as a fold in rank order 0..P-1 that
- *     starts from rank 0's value and accumulates in fp32 (bf16 inputs are
- *     widened exactly, the fp32 result is rounded to bf16 once, to nearest
- *     even; int32 sums wrap).  min and max keep the earlier rank's value on a
+ *     starts from rank 0's value and accumulates in fp32 (bf16 and fp16
+ *     inputs are widened exactly, the fp32 result is rounded back once, to
+ *     nearest even; int32 sums wrap).  min and max keep the earlier rank's value on a
  *     tie.  Results therefore do not depend on the launch configuration.
  *     [digest] s2.1 gives the op set (add, min, max); the order and
  *     accumulator type are this library's choice, fixed so results are
@@ -54,7 +54,7 @@ typedef enum {
     CCL_ERR_NOMEM = 6        /* host or device allocation for library state failed */
 } ccl_status_t;
 
-typedef enum { CCL_FLOAT32 = 0, CCL_BFLOAT16 = 1, CCL_INT32 = 2 } ccl_dtype_t;
+typedef enum { CCL_FLOAT32 = 0, CCL_BFLOAT16 = 1, CCL_INT32 = 2, CCL_FLOAT16 = 3 } ccl_dtype_t;
 
 /* [digest] s2.1: the reduction operations the bulk-reduce primitive offers. */
 typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
@@ -161,6 +161,34 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
 ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nranks,
                             size_t sendcount, int dtype, void *stream,
                             const ccl_launch_config_t *cfg);
+
+/*
+ * Reduce ([roadmap] GENK section: ring reduce; [digest] s2.2: shard-in with a
+ * single owner).  For i < count: recv[i] = fold over r of send[r][i].
+ *
+ *   send   P pointers, each to `count` elements.
+ *   recv   the root's output buffer, `count` elements.
+ *   root   the rank that owns recv, 0 <= root < P (it does not change the
+ *          result: on one GPU every rank's buffer is addressable).
+ *   In place: recv == send[r] is allowed (NCCL's in-place form is r = root);
+ *   any other overlap gives CCL_ERR_ALIASING.
+ */
+ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t count, int dtype,
+                        int op, int root, void *stream, const ccl_launch_config_t *cfg);
+
+/*
+ * Broadcast ([roadmap] GENK section: ring broadcast; [digest] s2.2: shard-out
+ * from a single owner, one load serving every destination).  For q < P and
+ * i < count: recv[q][i] = send[i].
+ *
+ *   send   the root's buffer, `count` elements.
+ *   recv   P pointers, each to `count` elements.
+ *   root   the rank that owns send, 0 <= root < P.
+ *   In place: recv[q] == send is allowed (NCCL's form is q = root); other
+ *   overlaps give CCL_ERR_ALIASING.  dtype only sets the element size.
+ */
+ccl_status_t ccl_broadcast(const void *send, void *const *recv, int nranks, size_t count,
+                           int dtype, int root, void *stream, const ccl_launch_config_t *cfg);
 
 /* ------------------------------------------------------------------ reshard
  * Layout-aware M-to-N reshard ([digest] s1.2 and s1.3): a tensor laid out

@@ -7,7 +7,7 @@ scalar C, ``-O2 -fno-fast-math -ffp-contract=off``).
 
 What each call computes, with the passages it follows, is documented in
 ``ccl_oracle.c``.  Arrays are numpy: ``f32`` -> float32, ``i32`` -> int32,
-``bf16`` -> uint16 holding the bf16 bit pattern.
+``bf16`` / ``f16`` -> uint16 holding the bit pattern.
 
 Layouts for reshard are ``(mesh_dims, start_rank, placements)`` where each
 placement is ``"R"`` (Replicate) or ``("S", d)`` (Shard along tensor dim d),
@@ -26,7 +26,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ccl_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DTYPES = {"f32": (0, np.float32), "bf16": (1, np.uint16), "i32": (2, np.int32)}
+DTYPES = {"f32": (0, np.float32), "bf16": (1, np.uint16), "i32": (2, np.int32),
+          "f16": (3, np.uint16)}
 OPS = {"sum": 0, "min": 1, "max": 2}
 
 _lib = None
@@ -59,6 +60,8 @@ def _load():
         lib.orc_reduce_scatter.argtypes = [pp, pp, i32, sz, i32, i32]
         lib.orc_all_gather.argtypes = [pp, pp, i32, sz, i32]
         lib.orc_fold_at.argtypes = [pp, i32, i32, i32, pu64, sz, vp]
+        lib.orc_reduce.argtypes = [pp, vp, i32, sz, i32, i32]
+        lib.orc_broadcast.argtypes = [vp, pp, i32, sz, i32]
         lay = [i32, p64, i64, pint, pint]
         lib.orc_reshard.argtypes = [i32, p64, i32] + lay + lay + [pp, pp]
         lib.orc_reshard_at.argtypes = [i32, p64, i32] + lay + lay + [pp, i64, pu64, sz, vp]
@@ -68,8 +71,12 @@ def _load():
         lib.orc_narrow_bf16.restype = ctypes.c_uint16
         lib.orc_widen_bf16.argtypes = [ctypes.c_uint16]
         lib.orc_widen_bf16.restype = ctypes.c_float
+        lib.orc_narrow_f16.argtypes = [ctypes.c_float]
+        lib.orc_narrow_f16.restype = ctypes.c_uint16
+        lib.orc_widen_f16.argtypes = [ctypes.c_uint16]
+        lib.orc_widen_f16.restype = ctypes.c_float
         for f in ("orc_all_reduce", "orc_reduce_scatter", "orc_all_gather", "orc_fold_at",
-                  "orc_reshard", "orc_reshard_at"):
+                  "orc_reshard", "orc_reshard_at", "orc_reduce", "orc_broadcast"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -122,6 +129,22 @@ def all_gather(xs, dtype: str):
     P, m = len(xs), xs[0].size
     ys = [np.empty(P * m, npdt) for _ in range(P)]
     _rc(_load().orc_all_gather(_ptrs(xs), _ptrs(ys), P, m, code), "all_gather")
+    return ys
+
+
+def reduce(xs, dtype: str, op: str = "sum"):
+    """The root's output of a reduce: the fold of all P inputs."""
+    code, npdt, xs = _check_bufs(xs, dtype)
+    y = np.empty(xs[0].size, npdt)
+    _rc(_load().orc_reduce(_ptrs(xs), y.ctypes.data, len(xs), xs[0].size, code, OPS[op]), "reduce")
+    return y
+
+
+def broadcast(x, P: int, dtype: str):
+    """Every rank's output of a broadcast from one root buffer."""
+    code, npdt, (x,) = _check_bufs([x], dtype)
+    ys = [np.empty(x.size, npdt) for _ in range(P)]
+    _rc(_load().orc_broadcast(x.ctypes.data, _ptrs(ys), P, x.size, code), "broadcast")
     return ys
 
 
@@ -216,3 +239,11 @@ def narrow_bf16(x: float) -> int:
 
 def widen_bf16(h: int) -> float:
     return float(_load().orc_widen_bf16(int(h)))
+
+
+def narrow_f16(x: float) -> int:
+    return int(_load().orc_narrow_f16(float(x)))
+
+
+def widen_f16(h: int) -> float:
+    return float(_load().orc_widen_f16(int(h)))

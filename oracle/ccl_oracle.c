@@ -19,7 +19,8 @@
  * Readings the pages leave open (each also listed in the design notes):
  *   - Reduction is a fold in rank order 0..P-1 that starts from rank 0's
  *     value, accumulates in fp32 (int32 wraps), and narrows once at the end.
- *   - bf16 narrowing is round-to-nearest-even; a NaN becomes 0x7FC0.
+ *   - bf16 and fp16 narrowing are round-to-nearest-even; a NaN becomes
+ *     0x7FC0 (bf16) or 0x7E00 (fp16).
  *   - min keeps the earlier operand unless the later one is strictly smaller;
  *     max likewise with strictly greater (so ties, including +0/-0, keep the
  *     earlier rank's value).
@@ -40,6 +41,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_I32 2
+#define ORC_F16 3
 #define ORC_SUM 0
 #define ORC_MIN 1
 #define ORC_MAX 2
@@ -73,11 +75,44 @@ static uint16_t orc_bf16_narrow(float f) {
     return (uint16_t)(u >> 16);
 }
 
+/* IEEE binary16 -> binary32 is exact (every half value is a float value). */
+static float orc_f16_widen(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+    if (e == 0x1f) return bits_to_f32(sign | 0x7f800000u | (m << 13)); /* inf / NaN */
+    if (e != 0) return bits_to_f32(sign | ((e + 112u) << 23) | (m << 13));
+    /* zero or subnormal: m * 2^-24, exact in fp32 */
+    float v = (float)m * bits_to_f32(0x33800000u); /* 2^-24 */
+    return sign ? -v : v;
+}
+
+/* binary32 -> binary16, round to nearest, ties to even; NaN -> 0x7e00. */
+static uint16_t orc_f16_narrow(float f) {
+    uint32_t u = f32_to_bits(f);
+    uint32_t sign = (u >> 16) & 0x8000u;
+    uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return (uint16_t)0x7e00u;
+    if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u); /* >= 65520 rounds to inf */
+    if (a >= 0x38800000u) {                                  /* normal half: >= 2^-14 */
+        uint32_t r = a + 0xfffu + ((a >> 13) & 1u);          /* round at bit 13 */
+        r -= (uint32_t)(127 - 15) << 23;                     /* rebias the exponent */
+        return (uint16_t)(sign | (r >> 13));
+    }
+    if (a <= 0x33000000u) return (uint16_t)sign; /* <= 2^-25 rounds to zero (tie to even) */
+    /* subnormal half: k = value / 2^-24 = mant * 2^(e - 126), rounded to nearest even */
+    uint32_t e = a >> 23;
+    uint32_t mant = (a & 0x7fffffu) | 0x800000u;
+    uint32_t s = 126u - e; /* 14 .. 24 */
+    uint32_t k = (mant + (1u << (s - 1)) - 1u + ((mant >> s) & 1u)) >> s;
+    return (uint16_t)(sign | k);
+}
+
 static int dtype_size(int dtype) {
     switch (dtype) {
     case ORC_F32: return 4;
     case ORC_BF16: return 2;
     case ORC_I32: return 4;
+    case ORC_F16: return 2;
     default: return 0;
     }
 }
@@ -119,7 +154,7 @@ static void fold_element(const void *const *x, int P, int dtype, int op, size_t 
             acc = fold_f32(acc, v, op);
         }
         memcpy(dst, &acc, 4);
-    } else {
+    } else if (dtype == ORC_BF16) {
         uint16_t h;
         memcpy(&h, (const char *)x[0] + i * 2, 2);
         float acc = orc_bf16_widen(h);
@@ -128,6 +163,16 @@ static void fold_element(const void *const *x, int P, int dtype, int op, size_t 
             acc = fold_f32(acc, orc_bf16_widen(h), op);
         }
         h = orc_bf16_narrow(acc);
+        memcpy(dst, &h, 2);
+    } else {
+        uint16_t h;
+        memcpy(&h, (const char *)x[0] + i * 2, 2);
+        float acc = orc_f16_widen(h);
+        for (int r = 1; r < P; ++r) {
+            memcpy(&h, (const char *)x[r] + i * 2, 2);
+            acc = fold_f32(acc, orc_f16_widen(h), op);
+        }
+        h = orc_f16_narrow(acc);
         memcpy(dst, &h, 2);
     }
 }
@@ -187,6 +232,32 @@ int orc_all_gather(const void *const *send, void *const *recv, int P, size_t sen
             for (size_t j = 0; j < sendcount; ++j)
                 memcpy((char *)recv[q] + ((size_t)r * sendcount + j) * s,
                        (const char *)send[r] + j * s, s);
+    return 0;
+}
+
+/*
+ * Reduce: the single-owner form of the shard-in -- the root's buffer receives
+ * the rank-order fold of all P inputs ([roadmap] GENK section: ring reduce;
+ * [digest] s2.2: the owner reduces locally).
+ */
+int orc_reduce(const void *const *send, void *recv, int P, size_t count, int dtype, int op) {
+    if (check_common(send, P, dtype, op) || !recv) return -1;
+    const int s = dtype_size(dtype);
+    for (size_t i = 0; i < count; ++i) fold_element(send, P, dtype, op, i, (char *)recv + i * s);
+    return 0;
+}
+
+/*
+ * Broadcast: the single-owner form of the shard-out -- every rank's buffer
+ * receives the root's buffer ([roadmap] GENK section: ring broadcast;
+ * [digest] s2.2: one load serves every destination).
+ */
+int orc_broadcast(const void *send, void *const *recv, int P, size_t count, int dtype) {
+    if (!send || !recv || P < 1 || dtype_size(dtype) == 0) return -1;
+    const size_t s = (size_t)dtype_size(dtype);
+    for (int q = 0; q < P; ++q)
+        for (size_t i = 0; i < count; ++i)
+            memcpy((char *)recv[q] + i * s, (const char *)send + i * s, s);
     return 0;
 }
 
@@ -430,6 +501,8 @@ int64_t orc_local_numel(int ndim, const int64_t *shape, int m_ndims, const int64
     return n;
 }
 
-/* Exposed for tests of the rounding rule itself. */
+/* Exposed for tests of the rounding rules themselves. */
 uint16_t orc_narrow_bf16(float f) { return orc_bf16_narrow(f); }
 float orc_widen_bf16(uint16_t h) { return orc_bf16_widen(h); }
+uint16_t orc_narrow_f16(float f) { return orc_f16_narrow(f); }
+float orc_widen_f16(uint16_t h) { return orc_f16_widen(h); }

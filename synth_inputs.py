@@ -4,7 +4,8 @@ This module only draws numbers: it holds none of the collectives' arithmetic.
 Every draw uses numpy's PCG64 ``default_rng(seed)``; rank r's buffer is the
 r-th draw of N values from one generator (rank-major order).  bf16 buffers are
 fp32 draws converted by PyTorch's CPU ``to(torch.bfloat16)`` (round to nearest
-even) and returned as uint16 bit patterns.
+even) and returned as uint16 bit patterns; fp16 buffers likewise through numpy's
+``astype(float16)``.
 
 Distributions (the workloads the reduce/copy data plane is measured on):
   ``uniform``  2*U - 1 with U ~ U[0,1) in float32, i.e. values in [-1, 1)
@@ -16,7 +17,7 @@ from __future__ import annotations
 
 import numpy as np
 
-NP_TYPES = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
+NP_TYPES = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f16": np.uint16}
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -55,6 +56,8 @@ def _draw(rng: np.random.Generator, dist: str, n: int, dtype: str) -> np.ndarray
         return x
     if dtype == "bf16":
         return to_bf16_bits(x)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
     if dtype == "i32":
         raise ValueError("float draws cannot fill int32 buffers")
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -3,7 +3,7 @@
 The bar:
   * int32, min/max and every copy: bit-exact.
   * fp32 sum: bit-equal, or |got - want| <= 1e-6 * max(|want|, 2^-126).
-  * bf16 sum: the two bf16 values are at most 1 ulp apart (their
+  * bf16 and fp16 sum: the two values are at most 1 ulp apart (their
     sign-magnitude ordinals differ by <= 1).
 Both sides fold in fp32 in rank order 0..P-1, so bit equality is expected;
 the tolerance is the stated bar, and non-bit-equal counts are reported.
@@ -24,8 +24,9 @@ def _ordinal_bf16(h: np.ndarray) -> np.ndarray:
 def assert_parity(got: np.ndarray, want: np.ndarray, dtype: str, op: str, what: str = "") -> int:
     """Assert the bar; returns the number of elements that are not bit-equal."""
     assert got.shape == want.shape, f"{what}: shape {got.shape} vs {want.shape}"
-    gb = got.view(np.uint16 if dtype == "bf16" else np.uint32)
-    wb = want.view(np.uint16 if dtype == "bf16" else np.uint32)
+    half = dtype in ("bf16", "f16")
+    gb = got.view(np.uint16 if half else np.uint32)
+    wb = want.view(np.uint16 if half else np.uint32)
     neq = gb != wb
     n_neq = int(np.count_nonzero(neq))
     if n_neq == 0:

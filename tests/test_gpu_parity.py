@@ -19,8 +19,8 @@ from collective_communication_plane_amd import ccl
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-NP = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32}
-ESZ = {"f32": 4, "bf16": 2, "i32": 4}
+NP = {"f32": np.float32, "bf16": np.uint16, "i32": np.int32, "f16": np.uint16}
+ESZ = {"f32": 4, "bf16": 2, "i32": 4, "f16": 2}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -57,7 +57,7 @@ def run_ar(xs, dtype, op, offset=0, cfg=None, out_offset=None):
 # ------------------------------------------------------------- all-reduce
 
 @pytest.mark.parametrize("P", [1, 2, 3, 5, 8, 16])
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32", "f16"])
 @pytest.mark.parametrize("op", ["sum", "min", "max"])
 def test_all_reduce_matches_oracle(P, dtype, op):
     n = 3 * 16384 + 5  # several 64 KiB chunks plus a ragged tail
@@ -183,7 +183,7 @@ def run_rs(xs, dtype, op, offset=0, cfg=None, out_offset=None):
 
 
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32", "f16"])
 @pytest.mark.parametrize("op", ["sum", "min", "max"])
 @pytest.mark.parametrize("m", [1, 13, 3 * 8192 + 3])
 def test_reduce_scatter_matches_oracle(P, dtype, op, m):
@@ -233,7 +233,7 @@ def run_ag(xs, dtype, offset=0, cfg=None, out_offset=None):
 
 
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32", "f16"])
 @pytest.mark.parametrize("m", [1, 9, 3 * 8192 + 1])
 def test_all_gather_matches_oracle(P, dtype, m):
     xs = si.rank_buffers(P, m, dtype, dist_of(dtype), seed=P * m)
@@ -455,3 +455,82 @@ def test_default_launch_for_every_rank_count(P):
     want = oracle.all_reduce(xs, "bf16", "sum")
     for q in range(P):
         assert_parity(got[q], want[q], "bf16", "sum", f"AR default P={P}")
+
+
+# ---------------------------------------------------------- reduce / broadcast
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16", "i32"])
+@pytest.mark.parametrize("op", ["sum", "min", "max"])
+def test_reduce_matches_oracle(P, dtype, op):
+    n = 2 * 8192 + 11
+    xs = si.rank_buffers(P, n, dtype, dist_of(dtype), seed=P + 3)
+    dx = upload_all(xs, DEV)
+    dy = DevBuf(n * ESZ[dtype], DEV)
+    root = P - 1
+    ccl.check(ccl.ccl_reduce([b.ptr for b in dx], dy.ptr, P, n, ccl.DTYPES[dtype], ccl.OPS[op],
+                             root, stream()), "reduce")
+    torch.cuda.synchronize()
+    assert dy.guards_intact()
+    assert_parity(dy.download(NP[dtype]), oracle.reduce(xs, dtype, op), dtype, op, f"reduce P={P}")
+
+
+@pytest.mark.parametrize("P", [1, 2, 5, 8, 16])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n", [1, 7, 3 * 8192 + 5])
+def test_broadcast_matches_oracle(P, dtype, n):
+    x = si.rank_buffers(1, n, dtype, "normal", seed=n)[0]
+    dx = DevBuf(x.nbytes, DEV).upload(x)
+    dy = [DevBuf(x.nbytes, DEV) for _ in range(P)]
+    ccl.check(ccl.ccl_broadcast(dx.ptr, [b.ptr for b in dy], P, n, ccl.DTYPES[dtype], 0, stream()),
+              "broadcast")
+    torch.cuda.synchronize()
+    want = oracle.broadcast(x, P, dtype)
+    for q in range(P):
+        assert dy[q].guards_intact()
+        np.testing.assert_array_equal(dy[q].download(NP[dtype]), want[q])
+
+
+def test_reduce_and_broadcast_in_place_and_offsets():
+    P, n = 8, 40003
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=50)
+    want = oracle.reduce(xs, "bf16", "sum")
+    # in place on the root's send buffer
+    dx = upload_all(xs, DEV)
+    ccl.check(ccl.ccl_reduce([b.ptr for b in dx], dx[3].ptr, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                             3, stream()))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dx[3].download(np.uint16), want)
+    # inputs at offset 2, output aligned: realigned path
+    dx = [DevBuf(x.nbytes, DEV, 2).upload(x) for x in xs]
+    dy = DevBuf(n * 2, DEV)
+    ccl.check(ccl.ccl_reduce([b.ptr for b in dx], dy.ptr, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                             0, stream()))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dy.download(np.uint16), want)
+    # broadcast in place at the root, the others at assorted offsets
+    x = xs[0]
+    outs = [DevBuf(x.nbytes, DEV, o) for o in (0, 2, 4, 6, 8, 10, 12, 14)]
+    outs[5].upload(x)
+    st = ccl.ccl_broadcast(outs[5].ptr, [b.ptr for b in outs], P, n, ccl.CCL_BFLOAT16, 5, stream())
+    ccl.check(st)
+    torch.cuda.synchronize()
+    for b in outs:
+        np.testing.assert_array_equal(b.download(np.uint16), x)
+
+
+def test_reduce_and_broadcast_reject_bad_arguments():
+    P, n = 4, 100
+    bufs = [DevBuf(n * 4, DEV) for _ in range(P)]
+    ptrs = [b.ptr for b in bufs]
+    assert ccl.ccl_reduce(ptrs, ptrs[0], P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM, P, stream()) == \
+        ccl.CCL_ERR_INVALID_ARG  # root out of range
+    assert ccl.ccl_reduce(ptrs, ptrs[0] + 4, P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM, 0, stream()) == \
+        ccl.CCL_ERR_ALIASING
+    assert ccl.ccl_broadcast(ptrs[0], ptrs, P, n, ccl.CCL_FLOAT32, -1, stream()) == \
+        ccl.CCL_ERR_INVALID_ARG
+    assert ccl.ccl_broadcast(ptrs[0] + 8, ptrs, P, n, ccl.CCL_FLOAT32, 0, stream()) == \
+        ccl.CCL_ERR_ALIASING
+    torch.cuda.synchronize()
+    for b in bufs:
+        assert (b.base == b.fill).all().item()

@@ -379,3 +379,81 @@ def test_reshard_rejects_invalid_layouts(bad):
 
 def test_torch_available_for_library_checks():
     assert torch.tensor([1.0], dtype=torch.bfloat16).item() == 1.0
+
+
+# ------------------------------------------------------------- fp16
+
+@pytest.mark.parametrize(
+    "f32_pattern, f16_pattern",
+    [
+        (0x3F800000, 0x3C00),  # 1.0
+        (0x3F801000, 0x3C00),  # 1 + 2^-11: halfway, even below -> stays
+        (0x3F803000, 0x3C02),  # 1 + 3*2^-11: halfway, odd below -> up to even
+        (0x3F801001, 0x3C01),  # just above halfway -> up
+        (0x477FE000, 0x7BFF),  # 65504, the largest half
+        (0x477FEFFF, 0x7BFF),  # just below the overflow tie
+        (0x477FF000, 0x7C00),  # 65520: tie between 65504 and 2^16 -> even -> inf
+        (0x38800000, 0x0400),  # 2^-14, the smallest normal half
+        (0x387FC000, 0x03FF),  # 1023 * 2^-24, the largest subnormal
+        (0x33800000, 0x0001),  # 2^-24, the smallest subnormal
+        (0x33000000, 0x0000),  # 2^-25: tie between 0 and 2^-24 -> 0
+        (0x33000001, 0x0001),  # just above -> 2^-24
+        (0x33C00000, 0x0002),  # 1.5 * 2^-24: tie between 1 and 2 -> 2
+        (0xC0000000, 0xC000),  # -2
+        (0x80000000, 0x8000),  # -0
+        (0x7F800000, 0x7C00),  # +inf
+        (0x7FC00001, 0x7E00),  # NaN -> canonical
+    ],
+)
+def test_f16_rne_hand_worked(f32_pattern, f16_pattern):
+    assert oracle.narrow_f16(bits_f32(f32_pattern)) == f16_pattern
+
+
+def test_f16_narrow_and_widen_match_numpy():
+    rng = np.random.default_rng(11)
+    # values spread over the whole half range, subnormals and overflow included
+    mags = np.exp2(rng.uniform(-27, 17, size=20000)).astype(np.float32)
+    x = (mags * rng.choice([-1, 1], size=mags.size)).astype(np.float32)
+    with np.errstate(over="ignore"):  # values past 65520 become inf on purpose
+        want = x.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.narrow_f16(float(v)) for v in x], np.uint16)
+    np.testing.assert_array_equal(got, want)
+    h = np.arange(0, 2**16, 7, dtype=np.uint16)
+    h = h[~np.isnan(h.view(np.float16))]
+    wide = np.array([oracle.widen_f16(int(v)) for v in h], np.float32)
+    np.testing.assert_array_equal(wide.view(np.uint32), h.view(np.float16).astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("P", PS)
+def test_allreduce_f16_sum_equals_fp32_fold_then_numpy_rne(P):
+    xs = [x.astype(np.float16).view(np.uint16) for x in si.rank_buffers(P, 4000, "f32", "normal", seed=P)]
+    ys = oracle.all_reduce(xs, "f16", "sum")
+    want = seq_sum_f32([x.view(np.float16).astype(np.float32) for x in xs]).astype(np.float16)
+    np.testing.assert_array_equal(ys[0], want.view(np.uint16))
+
+
+# ------------------------------------------------------ reduce / broadcast
+
+@pytest.mark.parametrize("P", PS)
+@pytest.mark.parametrize("dtype,op", [("f32", "sum"), ("bf16", "max"), ("i32", "sum"), ("f16", "min")])
+def test_reduce_is_the_fold_into_one_buffer(P, dtype, op):
+    if dtype == "f16":
+        xs = [x.astype(np.float16).view(np.uint16) for x in si.rank_buffers(P, 999, "f32", "uniform", seed=3)]
+    else:
+        xs = si.rank_buffers(P, 999, dtype, "int20" if dtype == "i32" else "uniform", seed=3)
+    y = oracle.reduce(xs, dtype, op)
+    if dtype == "f32" and op == "sum":
+        np.testing.assert_array_equal(y, seq_sum_f32(xs))
+    elif dtype == "i32":
+        np.testing.assert_array_equal(y, np.sum(np.stack(xs).astype(np.int64), 0).astype(np.int32))
+    elif dtype == "bf16":
+        np.testing.assert_array_equal(y, si.to_bf16_bits(np.maximum.reduce([si.bf16_bits_to_f32(x) for x in xs])))
+    else:
+        np.testing.assert_array_equal(y, np.minimum.reduce([x.view(np.float16) for x in xs]).view(np.uint16))
+
+
+@pytest.mark.parametrize("P", PS)
+def test_broadcast_copies_the_root_buffer_everywhere(P):
+    x = si.rank_buffers(1, 1001, "bf16", "normal", seed=P)[0]
+    for y in oracle.broadcast(x, P, "bf16"):
+        np.testing.assert_array_equal(y, x)
