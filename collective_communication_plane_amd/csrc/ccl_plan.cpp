@@ -4,9 +4,11 @@
 // descriptors, only intersecting intervals are moved, leaders are balanced),
 // s1.3 (Mesh / Shard / Replicate and the layout constraints).
 //
-// A layout with Shard(d) on mesh axis k splits tensor dim d into dims[k]
-// equal blocks; mesh rank l (row-major coordinates c) holds block c[k] and is
-// a replica of every other rank with the same c[k].  With no Shard axis, every
+// A layout with Shard(d) on mesh axis k splits tensor dim d into blocks of
+// ceil(D / dims[k]) indices, clipped to D so trailing blocks may be short or
+// empty (the torch.chunk convention; the pages leave uneven splits open);
+// mesh rank l (row-major coordinates c) holds block c[k] and is a replica of
+// every other rank with the same c[k].  With no Shard axis, every
 // rank holds the whole tensor.  Each distinct block ("shard") is a box of
 // global indices; the plan intersects every destination shard with every
 // source shard and emits the intersection as maximal runs that are
@@ -56,7 +58,6 @@ ccl_status_t make_layout(const ccl_mesh_t *m, const ccl_placement_t *pl, int ndi
     if (pl[k].kind != CCL_SHARD) return CCL_ERR_INVALID_ARG;
     if (pl[k].dim < 0 || pl[k].dim >= ndim) return CCL_ERR_INVALID_ARG;
     if (L->shard_axis >= 0) return CCL_ERR_LAYOUT;  // at most one sharded mesh axis
-    if (shape[pl[k].dim] % m->dims[k]) return CCL_ERR_LAYOUT;  // uneven blocks
     L->shard_axis = k;
     L->shard_dim = pl[k].dim;
     L->parts = m->dims[k];
@@ -79,10 +80,17 @@ void shard_box(const Layout &L, int64_t t, int ndim, const int64_t *shape, int64
     hi[d] = shape[d];
   }
   if (L.shard_axis >= 0) {
-    const int64_t part = shape[L.shard_dim] / L.parts;
-    lo[L.shard_dim] = t * part;
-    hi[L.shard_dim] = (t + 1) * part;
+    const int64_t D = shape[L.shard_dim];
+    const int64_t part = (D + L.parts - 1) / L.parts;
+    lo[L.shard_dim] = std::min(t * part, D);
+    hi[L.shard_dim] = std::min(lo[L.shard_dim] + part, D);
   }
+}
+
+uint64_t box_volume(const int64_t *lo, const int64_t *hi, int ndim) {
+  uint64_t n = 1;
+  for (int d = 0; d < ndim; ++d) n *= (uint64_t)(hi[d] - lo[d]);
+  return n;
 }
 
 int64_t rowmajor_offset(const int64_t *g, const int64_t *lo, const int64_t *hi, int ndim) {
@@ -128,10 +136,17 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
   p->n_dst = D.size;
   p->n_dst_shards = (int32_t)D.parts;
 
-  const uint64_t src_bytes = numel / (uint64_t)S.parts * esz;
-  const uint64_t dst_bytes = numel / (uint64_t)D.parts * esz;
-  p->src_local_bytes.assign(S.size, src_bytes);
-  p->dst_local_bytes.assign(D.size, dst_bytes);
+  int64_t blo[CCL_MAX_TENSOR_DIMS], bhi[CCL_MAX_TENSOR_DIMS];
+  p->src_local_bytes.resize(S.size);
+  for (int l = 0; l < S.size; ++l) {
+    shard_box(S, shard_of(S, l), ndim, shape, blo, bhi);
+    p->src_local_bytes[l] = box_volume(blo, bhi, ndim) * esz;
+  }
+  p->dst_local_bytes.resize(D.size);
+  for (int l = 0; l < D.size; ++l) {
+    shard_box(D, shard_of(D, l), ndim, shape, blo, bhi);
+    p->dst_local_bytes[l] = box_volume(blo, bhi, ndim) * esz;
+  }
 
   // Source holder of each source shard: its lowest rank (all replicas agree).
   std::vector<int32_t> src_holder(S.parts, -1);

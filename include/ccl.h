@@ -201,7 +201,8 @@ ccl_status_t ccl_broadcast(const void *send, void *const *recv, int nranks, size
 
 typedef enum { CCL_REPLICATE = 0, CCL_SHARD = 1 } ccl_placement_kind_t;
 
-/* Replicate(), or Shard(dim): dim is split into mesh-axis-size equal blocks. */
+/* Replicate(), or Shard(dim): dim is split into mesh-axis-size blocks of
+ * ceil(D / axis size) indices each (the last ones short or empty). */
 typedef struct {
     int32_t kind;
     int32_t dim;
@@ -243,9 +244,12 @@ typedef struct ccl_plan ccl_plan_t;
  * their loads differ by at most one).  Pure host code: no HIP call.
  *
  * Constraints ([digest] s1.3), each CCL_ERR_LAYOUT when broken: the meshes
- * are disjoint rank ranges; at most one mesh axis per layout is Shard; the
- * sharded tensor dim is divisible by that axis's size; every mesh has at most
- * CCL_MAX_MESH_RANKS ranks.  Malformed descriptors give CCL_ERR_INVALID_ARG.
+ * are disjoint rank ranges; at most one mesh axis per layout is Shard; every
+ * mesh has at most CCL_MAX_MESH_RANKS ranks.  Malformed descriptors give
+ * CCL_ERR_INVALID_ARG.  Shard(dim) over an axis of m ranks cuts the dim into
+ * blocks of ceil(D/m) indices; when m does not divide D the trailing blocks
+ * are shorter or empty (the torch.chunk convention), so local buffer sizes
+ * can differ between ranks (see ccl_plan_local_bytes).
  *
  * Intervals are maximal row-major runs, sorted by (dst_shard, dst_offset);
  * together they tile every destination shard exactly once.  *plan_out is

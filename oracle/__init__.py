@@ -65,7 +65,7 @@ def _load():
         lay = [i32, p64, i64, pint, pint]
         lib.orc_reshard.argtypes = [i32, p64, i32] + lay + lay + [pp, pp]
         lib.orc_reshard_at.argtypes = [i32, p64, i32] + lay + lay + [pp, i64, pu64, sz, vp]
-        lib.orc_local_numel.argtypes = [i32, p64, i32, p64, pint, pint]
+        lib.orc_local_numel.argtypes = [i32, p64, i32, p64, pint, pint, i64]
         lib.orc_local_numel.restype = i64
         lib.orc_narrow_bf16.argtypes = [ctypes.c_float]
         lib.orc_narrow_bf16.restype = ctypes.c_uint16
@@ -186,11 +186,12 @@ def mesh_size(layout) -> int:
     return int(np.prod(layout[0]))
 
 
-def local_numel(shape, layout) -> int:
+def local_numel(shape, layout, rank_index: int = 0) -> int:
+    """Elements held by the rank at position ``rank_index`` of the layout's mesh."""
     shp = np.array(shape, np.int64)
     args, _keep = _layout_args(layout)
     n = _load().orc_local_numel(len(shape), shp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                args[0], args[1], args[3], args[4])
+                                args[0], args[1], args[3], args[4], int(rank_index))
     if n < 0:
         raise ValueError("oracle: invalid layout")
     return int(n)
@@ -206,7 +207,7 @@ def reshard(shape, src_layout, dst_layout, src_bufs, fill=0):
     sa, k1 = _layout_args(src_layout)
     da, k2 = _layout_args(dst_layout)
     nd = mesh_size(dst_layout)
-    dst = [np.full(local_numel(shape, dst_layout), fill, dt) for _ in range(nd)]
+    dst = [np.full(local_numel(shape, dst_layout, l), fill, dt) for l in range(nd)]
     rc = _load().orc_reshard(len(shape), shp.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                              dt.itemsize, *sa, *da, _ptrs(src_bufs), _ptrs(dst))
     del k1, k2

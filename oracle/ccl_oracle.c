@@ -27,8 +27,9 @@
  *   - Mesh ranks are numbered row-major (last mesh axis fastest) from
  *     start_rank; placements[k] applies to mesh axis k (both pinned by
  *     Example A in [digest] s1.4).
- *   - Shard(d) over m parts splits dim d into m equal contiguous blocks and
- *     requires m to divide the dim.
+ *   - Shard(d) over m parts splits dim d into contiguous blocks of
+ *     ceil(D/m) indices; the trailing blocks may be shorter or empty (the
+ *     convention torch.chunk and DTensor use; the pages do not say).
  *
  * Every function returns 0 on success and a negative value on bad input.
  * Style: scalar loops, no SIMD intrinsics, no threads, no fast-math.
@@ -289,13 +290,13 @@ static int64_t layout_size(const orc_layout *L) {
 }
 
 static int layout_check(const orc_layout *L, int ndim, const int64_t *shape) {
+    (void)shape; /* any dim size is valid: uneven blocks are clipped */
     if (L->ndims < 1 || L->ndims > ORC_MAX_MESH_DIMS || L->start_rank < 0) return -1;
     for (int k = 0; k < L->ndims; ++k) {
         if (L->dims[k] < 1) return -1;
         if (L->kind[k] == 1) {
             int d = L->sdim[k];
             if (d < 0 || d >= ndim) return -1;
-            if (shape[d] % L->dims[k] != 0) return -2; /* uneven split */
             for (int k2 = 0; k2 < k; ++k2)
                 if (L->kind[k2] == 1 && L->sdim[k2] == d) return -1; /* same dim twice */
         } else if (L->kind[k] != 0) {
@@ -314,7 +315,8 @@ static void unravel_mesh(const orc_layout *L, int64_t l, int64_t *c) {
 }
 
 /* The index box [lo, hi) a mesh coordinate holds: Shard(d) on axis k cuts dim d
- * into dims[k] equal blocks and takes block c[k]; Replicate leaves it whole. */
+ * into blocks of ceil(D / dims[k]) indices and takes block c[k] (clipped to D,
+ * so late blocks can be short or empty); Replicate leaves the dim whole. */
 static void rank_box(const orc_layout *L, const int64_t *c, int ndim, const int64_t *shape,
                      int64_t *lo, int64_t *hi) {
     for (int d = 0; d < ndim; ++d) {
@@ -324,9 +326,9 @@ static void rank_box(const orc_layout *L, const int64_t *c, int ndim, const int6
     for (int k = 0; k < L->ndims; ++k) {
         if (L->kind[k] != 1) continue;
         int d = L->sdim[k];
-        int64_t part = shape[d] / L->dims[k];
-        lo[d] = c[k] * part;
-        hi[d] = lo[d] + part;
+        int64_t part = (shape[d] + L->dims[k] - 1) / L->dims[k];
+        lo[d] = c[k] * part < shape[d] ? c[k] * part : shape[d];
+        hi[d] = lo[d] + part < shape[d] ? lo[d] + part : shape[d];
     }
 }
 
@@ -487,14 +489,16 @@ int orc_reshard_at(int ndim, const int64_t *shape, int elem_size,
     return 0;
 }
 
-/* Number of elements a rank of a layout holds (its box volume). */
+/* Number of elements the l-th rank of a layout holds (its box volume). */
 int64_t orc_local_numel(int ndim, const int64_t *shape, int m_ndims, const int64_t *m_dims,
-                        const int *kind, const int *sdim) {
+                        const int *kind, const int *sdim, int64_t l) {
     orc_layout L;
     if (ndim < 1 || ndim > ORC_MAX_TENSOR_DIMS || !shape) return -1;
     if (fill_layout(&L, m_ndims, m_dims, 0, kind, sdim)) return -1;
     if (layout_check(&L, ndim, shape)) return -1;
-    int64_t c[ORC_MAX_MESH_DIMS] = {0}, lo[ORC_MAX_TENSOR_DIMS], hi[ORC_MAX_TENSOR_DIMS];
+    if (l < 0 || l >= layout_size(&L)) return -1;
+    int64_t c[ORC_MAX_MESH_DIMS], lo[ORC_MAX_TENSOR_DIMS], hi[ORC_MAX_TENSOR_DIMS];
+    unravel_mesh(&L, l, c);
     rank_box(&L, c, ndim, shape, lo, hi);
     int64_t n = 1;
     for (int d = 0; d < ndim; ++d) n *= hi[d] - lo[d];

@@ -10,7 +10,6 @@ query.
 from __future__ import annotations
 
 import gc
-import itertools
 
 import numpy as np
 import pytest
@@ -18,6 +17,7 @@ import torch
 
 import oracle
 import synth_inputs as si
+from _layout import local_blocks
 from _parity import DevBuf, upload_all
 from collective_communication_plane_amd import ccl
 
@@ -44,18 +44,6 @@ def make_plan(shape, dtype, src, dst):
     return plan
 
 
-def local_blocks(G, layout):
-    dims, _start, pl = layout
-    out = []
-    for c in itertools.product(*[range(m) for m in dims]):
-        blk = G
-        for k, p in enumerate(pl):
-            if p != "R":
-                blk = np.split(blk, dims[k], axis=p[1])[c[k]]
-        out.append(np.ascontiguousarray(blk).ravel())
-    return out
-
-
 CASES = [
     ((4, 8), ([1, 4], 0, ["R", ("S", 0)]), ([2, 2], 4, ["R", ("S", 0)])),   # Example A shape
     ((6, 4), ([2], 0, [("S", 0)]), ([1], 2, ["R"])),                        # Example B shape
@@ -66,6 +54,9 @@ CASES = [
     ((128, 33), ([2], 0, ["R"]), ([4], 2, [("S", 0)])),                     # scatter
     ((256, 256), ([4], 0, [("S", 0)]), ([4], 4, [("S", 0)])),               # identity
     ((512, 128), ([2, 4], 0, ["R", ("S", 1)]), ([4, 2], 8, [("S", 0), "R"])),
+    ((9, 8), ([4], 0, [("S", 0)]), ([3], 4, [("S", 0)])),                   # uneven, empty rank
+    ((10, 6), ([2, 2], 0, [("S", 0), "R"]), ([4], 4, [("S", 1)])),          # uneven columns
+    ((1001, 33), ([3], 0, [("S", 0)]), ([2, 3], 3, ["R", ("S", 1)])),       # ragged runs
 ]
 
 
@@ -186,3 +177,29 @@ def test_reshard_rw_b_full_size():
         want = full[:, 512 * d:512 * (d + 1), :].contiguous().view(torch.uint8).view(-1)
         assert torch.equal(ddst[d], want), d
     _sample_check(shape, src, dst, src_host, ddst)
+
+
+def test_example_b_two_pipeline_stages():
+    """Example B ([digest] s1.4): TP2,PP2 -> TP1,PP1 as one reshard per PP
+    stage.  In each stage's communicator the two trainer TP ranks (c-ranks 0,
+    1) hold the stage weight split on dim 0 and the generator joins as c-rank
+    2 with Replicate, so one plan serves both stages and the generator ends up
+    with both full stage weights."""
+    shape = (2048, 1536)
+    src = ([2], 0, [("S", 0)])
+    dst = ([1], 2, ["R"])
+    plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
+    try:
+        for stage in range(2):
+            W = si.tensor(shape, "bf16", "w002", seed=100 + stage)
+            halves = local_blocks(W, src)
+            dsrc = upload_all(halves, DEV)
+            ddst = [DevBuf(W.nbytes, DEV)]
+            ccl.check(ccl.ccl_reshard_copy(plan, [b.ptr for b in dsrc], [ddst[0].ptr],
+                                           torch.cuda.current_stream()))
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(ddst[0].download(np.uint16), W.ravel())
+            np.testing.assert_array_equal(ddst[0].download(np.uint16),
+                                          oracle.reshard(shape, src, dst, halves)[0])
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))

@@ -19,6 +19,7 @@ import torch
 import oracle
 import synth_inputs as si
 from _golden import load_example
+from _layout import chunk_piece, local_blocks
 
 PS = [1, 2, 3, 4, 8]
 
@@ -247,21 +248,6 @@ def global_iota(shape):
     return np.arange(int(np.prod(shape)), dtype=np.int32).reshape(shape)
 
 
-def local_blocks(G, layout):
-    """Expected per-rank buffers from numpy splitting of the global tensor:
-    rank l of the mesh (row-major coordinates) takes, for every Shard(d) axis
-    k, the c_k-th of dims[k] equal np.split pieces along d."""
-    dims, _start, pl = layout
-    out = []
-    for c in itertools.product(*[range(m) for m in dims]):
-        blk = G
-        for k, p in enumerate(pl):
-            if p != "R":
-                blk = np.split(blk, dims[k], axis=p[1])[c[k]]
-        out.append(np.ascontiguousarray(blk).ravel())
-    return out
-
-
 @pytest.mark.parametrize("name", ["example_a.txt", "example_b.txt"])
 def test_reshard_worked_examples(name):
     ex = load_example(name)
@@ -309,13 +295,11 @@ def _tiny_layouts(ndim, shape):
             sharded = [p for p in pl if p != "R"]
             if len(sharded) > 1:
                 continue
-            ok = all(p == "R" or shape[p[1]] % dims[k] == 0 for k, p in enumerate(pl))
-            if ok:
-                yield dims, list(pl)
+            yield dims, list(pl)
 
 
-@pytest.mark.parametrize("shape", [(6,), (4, 6), (2, 3, 4)])
-def test_reshard_all_tiny_layouts_against_numpy_split(shape):
+@pytest.mark.parametrize("shape", [(6,), (4, 6), (2, 3, 4), (5,), (7, 3), (3, 5, 2)])
+def test_reshard_all_tiny_layouts_against_torch_chunk(shape):
     G = global_iota(shape)
     layouts = list(_tiny_layouts(len(shape), shape))
     rng = np.random.default_rng(len(shape))
@@ -368,7 +352,7 @@ def test_reshard_detects_disagreeing_source_replicas():
 
 @pytest.mark.parametrize("bad", [
     dict(src=([2], 0, [("S", 0)]), dst=([2], 1, ["R"])),      # overlapping meshes
-    dict(src=([3], 0, [("S", 0)]), dst=([1], 3, ["R"])),      # 3 does not divide 8
+    dict(src=([2, 2], 0, [("S", 0), ("S", 0)]), dst=([1], 4, ["R"])),  # one dim sharded twice
     dict(src=([2], 0, [("S", 5)]), dst=([1], 2, ["R"])),      # no such tensor dim
 ])
 def test_reshard_rejects_invalid_layouts(bad):
@@ -457,3 +441,22 @@ def test_broadcast_copies_the_root_buffer_everywhere(P):
     x = si.rank_buffers(1, 1001, "bf16", "normal", seed=P)[0]
     for y in oracle.broadcast(x, P, "bf16"):
         np.testing.assert_array_equal(y, x)
+
+
+def test_uneven_shard_blocks_follow_torch_chunk():
+    """9 rows over 4 ranks: pieces of ceil(9/4) = 3 rows, the last rank empty;
+    10 over 4: 3, 3, 3, 1."""
+    for D, want in [(9, [3, 3, 3, 0]), (10, [3, 3, 3, 1]), (3, [1, 1, 1, 0]), (1, [1, 0, 0, 0])]:
+        sizes = [oracle.local_numel((D, 2), ([4], 0, [("S", 0)]), l) // 2 for l in range(4)]
+        assert sizes == want
+        assert sizes == [chunk_piece(np.zeros((D, 2)), 4, 0, c).shape[0] for c in range(4)]
+
+
+def test_uneven_reshard_round_trip():
+    t = si.tensor((11, 7), "f32", "normal", seed=12)
+    a = ([3], 0, [("S", 0)])
+    b = ([2, 2], 3, [("S", 1), "R"])
+    c = ([1], 7, ["R"])
+    mid = oracle.reshard((11, 7), a, b, local_blocks(t, a))
+    back = oracle.reshard((11, 7), b, c, mid)
+    np.testing.assert_array_equal(back[0], t.ravel())
