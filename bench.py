@@ -16,9 +16,9 @@ Besides the headline value the line carries:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (single thread);
   rows          the other data-plane workloads (reduce-scatter bf16 and int32,
-                all-gather, the all-reduce through the LDS pipeline, the two
-                weight reshards), each timed the same way after a warmup of
-                at least half a second.
+                all-gather, the all-reduce through the LDS pipeline, the
+                all-reduce with fused RMSNorm, the two weight reshards), each
+                timed the same way after a warmup of at least half a second.
 
 Other modes:
   --sweep       the launch-configuration sweep (chunk bytes, stages, unroll,
@@ -178,6 +178,20 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     record("all_reduce_bf16_lds_pipeline", 2 * P * n * 2, ms,
            "all_reduce sum, P=8 x 134,217,728 bf16, LDS pipeline (2 stages, 4 KiB chunks, "
            "<= 2 workgroups per CU)")
+    del dx, dy
+    torch.cuda.empty_cache()
+
+    # all-reduce with RMSNorm fused between its halves: 16384 tokens x 8192 hidden
+    rows, hidden = 16384, 8192
+    dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=dev)
+    dy = [torch.empty_like(t) for t in dx]
+    gamma = torch.from_numpy(si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
+                             .view(np.int16).copy()).to(dev)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, gamma, 1e-6,
+                                                            ccl.CCL_BFLOAT16, stream)),
+               steps, warmup, stream, warm_s)
+    record("all_reduce_rmsnorm_bf16", 2 * P * rows * hidden * 2 + hidden * 2, ms,
+           "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16")
     del dx, dy
     torch.cuda.empty_cache()
 

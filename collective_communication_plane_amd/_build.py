@@ -13,7 +13,8 @@ OUT = os.path.join(PKG, "libccl.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["ccl_api.cpp", "ccl_plan.cpp", "ccl_collectives.hip", "ccl_reshard.hip"]
+SOURCES = ["ccl_api.cpp", "ccl_plan.cpp", "ccl_collectives.hip", "ccl_reshard.hip",
+           "ccl_rmsnorm.hip"]
 
 # ccl_coll_inst.hip is compiled once per (kind, element type) slice.
 INSTANCES = [

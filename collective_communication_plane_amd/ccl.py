@@ -85,6 +85,7 @@ _lib = None
 
 EXPORTS = [
     "ccl_all_reduce", "ccl_reduce_scatter", "ccl_all_gather", "ccl_reduce", "ccl_broadcast",
+    "ccl_all_reduce_rmsnorm",
     "ccl_reshard_plan",
     "ccl_reshard_copy", "ccl_plan_destroy", "ccl_plan_num_intervals", "ccl_plan_get_interval",
     "ccl_plan_local_bytes", "ccl_plan_num_dst_shards", "ccl_plan_shard_replicas",
@@ -112,6 +113,7 @@ def _load():
     lib.ccl_reduce_scatter.argtypes = [pp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_all_gather.argtypes = [pp, pp, i32, sz, i32, vp, pcfg]
     lib.ccl_reduce.argtypes = [pp, vp, i32, sz, i32, i32, i32, vp, pcfg]
+    lib.ccl_all_reduce_rmsnorm.argtypes = [pp, pp, i32, sz, sz, vp, ctypes.c_float, i32, vp, pcfg]
     lib.ccl_broadcast.argtypes = [vp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_reshard_plan.argtypes = [ctypes.POINTER(TensorDesc), ctypes.POINTER(Mesh),
                                      ctypes.POINTER(Placement), ctypes.POINTER(Mesh),
@@ -192,6 +194,13 @@ def ccl_all_gather(send, recv, nranks: int, sendcount: int, dtype: int, stream=N
     s, r = _ptr_array(send), _ptr_array(recv)
     return _load().ccl_all_gather(_pp(s), _pp(r), nranks, sendcount, dtype, _stream(stream),
                                   _cfg(cfg))
+
+
+def ccl_all_reduce_rmsnorm(send, recv, nranks: int, rows: int, hidden: int, gamma, eps: float,
+                           dtype: int, stream=None, cfg=None) -> int:
+    s, r = _ptr_array(send), _ptr_array(recv)
+    return _load().ccl_all_reduce_rmsnorm(_pp(s), _pp(r), nranks, rows, hidden, _addr(gamma),
+                                          float(eps), dtype, _stream(stream), _cfg(cfg))
 
 
 def ccl_reduce(send, recv, nranks: int, count: int, dtype: int, op: int, root: int = 0,

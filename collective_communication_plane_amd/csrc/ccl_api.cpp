@@ -195,6 +195,43 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
 
+ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, int nranks,
+                                    size_t rows, size_t hidden, const void *gamma, float eps,
+                                    int dtype, void *stream, const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AR, nranks, &l);
+  if (st) return st;
+  if (nranks < 1 || nranks > CCL_MAX_RANKS) return CCL_ERR_INVALID_ARG;
+  if (dtype != CCL_FLOAT32 && dtype != CCL_BFLOAT16 && dtype != CCL_FLOAT16)
+    return CCL_ERR_INVALID_ARG;
+  if (!(eps >= 0.f) || eps > 1.f) return CCL_ERR_INVALID_ARG;  // also rejects NaN
+  if (rows == 0) return CCL_OK;
+  if (hidden == 0) return CCL_ERR_INVALID_ARG;
+  const uint64_t sz = dtype_size(dtype);
+  if (mul_overflows(hidden, sz) || mul_overflows(hidden * sz, rows)) return CCL_ERR_INVALID_ARG;
+  if ((hidden * sz) % ccl::kVecBytes) return CCL_ERR_UNSUPPORTED;  // rows of whole vectors
+  if (hidden * sz / ccl::kVecBytes > (uint64_t)ccl::kRmsMaxRowVecs) return CCL_ERR_UNSUPPORTED;
+  if (!send || !recv || !gamma || (uintptr_t)gamma % ccl::kVecBytes) return CCL_ERR_INVALID_ARG;
+  for (int r = 0; r < nranks; ++r) {
+    if (!send[r] || !recv[r]) return CCL_ERR_INVALID_ARG;
+    if ((uintptr_t)send[r] % ccl::kVecBytes || (uintptr_t)recv[r] % ccl::kVecBytes)
+      return CCL_ERR_UNSUPPORTED;  // the fused kernel runs on 16-byte aligned rows only
+  }
+  const uint64_t bytes = rows * hidden * sz;
+  if ((st = check_outputs_disjoint(recv, nranks, bytes))) return st;
+  for (int q = 0; q < nranks; ++q) {
+    Range y{(uintptr_t)recv[q], (uintptr_t)recv[q] + bytes};
+    Range g{(uintptr_t)gamma, (uintptr_t)gamma + hidden * sz};
+    if (overlap(y, g)) return CCL_ERR_ALIASING;
+    for (int r = 0; r < nranks; ++r) {
+      Range x{(uintptr_t)send[r], (uintptr_t)send[r] + bytes};
+      if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
+    }
+  }
+  ccl::RmsDesc d{nranks, dtype, rows, hidden, eps, send, recv, gamma};
+  return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream);
+}
+
 ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t count, int dtype,
                         int op, int root, void *stream, const ccl_launch_config_t *cfg) {
   ccl::Launch l;

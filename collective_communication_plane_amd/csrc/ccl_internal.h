@@ -98,6 +98,20 @@ int device_cu_count(int dev);
 ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch *out);
 ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t stream);
 
+// All-reduce with a row-wise RMSNorm between its halves, all checks passed.
+struct RmsDesc {
+  int P;
+  int dtype;
+  uint64_t rows;
+  uint64_t hidden;
+  float eps;
+  const void *const *send;
+  void *const *recv;
+  const void *gamma;
+};
+constexpr int kRmsMaxRowVecs = 8 * kThreads;  // 16-byte vectors per row
+ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t stream);
+
 // ------------------------------------------------------------------ reshard
 
 struct PlanInterval {

@@ -163,6 +163,32 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
                             const ccl_launch_config_t *cfg);
 
 /*
+ * All-reduce with RMSNorm fused between its two halves ([roadmap]: the Device
+ * API example that fuses a Transformer RMSNorm with reduce-scatter and
+ * all-gather in one kernel).  Every rank buffer is a rows x hidden row-major
+ * matrix.  Per row t:
+ *   s[h]  = fold over r of send[r][t][h], rounded to dtype (the reduce-scatter
+ *           value);
+ *   inv   = 1 / sqrt(mean over h of s[h]^2 + eps), computed in fp32;
+ *   recv[q][t][h] = dtype(s[h] * inv * gamma[h]) for every q.
+ * This equals reduce-scatter, RMSNorm on each owner's rows, then all-gather,
+ * whenever each shard holds whole rows; here a workgroup owns whole rows, so
+ * no shard boundary is needed.  The sum of squares is accumulated in fp32 in
+ * a fixed order, so results are reproducible; against an exact norm the
+ * relative error is at most about (hidden/2 + 4) * 2^-24.
+ *
+ *   dtype  CCL_FLOAT32, CCL_BFLOAT16 or CCL_FLOAT16 (op is sum).
+ *   gamma  hidden elements of dtype, device memory, 16-byte aligned.
+ *   eps    0 <= eps <= 1.
+ *   Every send/recv buffer must be 16-byte aligned and hidden * element size
+ *   a multiple of 16, with hidden * element size <= 32 KiB
+ *   (else CCL_ERR_UNSUPPORTED).  In place recv[q] == send[q] is allowed.
+ */
+ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, int nranks,
+                                    size_t rows, size_t hidden, const void *gamma, float eps,
+                                    int dtype, void *stream, const ccl_launch_config_t *cfg);
+
+/*
  * Reduce ([roadmap] GENK section: ring reduce; [digest] s2.2: shard-in with a
  * single owner).  For i < count: recv[i] = fold over r of send[r][i].
  *

@@ -62,6 +62,7 @@ def _load():
         lib.orc_fold_at.argtypes = [pp, i32, i32, i32, pu64, sz, vp]
         lib.orc_reduce.argtypes = [pp, vp, i32, sz, i32, i32]
         lib.orc_broadcast.argtypes = [vp, pp, i32, sz, i32]
+        lib.orc_all_reduce_rmsnorm.argtypes = [pp, pp, i32, sz, sz, vp, ctypes.c_double, i32]
         lay = [i32, p64, i64, pint, pint]
         lib.orc_reshard.argtypes = [i32, p64, i32] + lay + lay + [pp, pp]
         lib.orc_reshard_at.argtypes = [i32, p64, i32] + lay + lay + [pp, i64, pu64, sz, vp]
@@ -76,7 +77,8 @@ def _load():
         lib.orc_widen_f16.argtypes = [ctypes.c_uint16]
         lib.orc_widen_f16.restype = ctypes.c_float
         for f in ("orc_all_reduce", "orc_reduce_scatter", "orc_all_gather", "orc_fold_at",
-                  "orc_reshard", "orc_reshard_at", "orc_reduce", "orc_broadcast"):
+                  "orc_reshard", "orc_reshard_at", "orc_reduce", "orc_broadcast",
+                  "orc_all_reduce_rmsnorm"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -145,6 +147,19 @@ def broadcast(x, P: int, dtype: str):
     code, npdt, (x,) = _check_bufs([x], dtype)
     ys = [np.empty(x.size, npdt) for _ in range(P)]
     _rc(_load().orc_broadcast(x.ctypes.data, _ptrs(ys), P, x.size, code), "broadcast")
+    return ys
+
+
+def all_reduce_rmsnorm(xs, rows: int, hidden: int, gamma, eps: float, dtype: str):
+    """All-reduce (sum) with a row-wise RMSNorm between the two halves."""
+    code, npdt, xs = _check_bufs(xs, dtype)
+    gamma = np.ascontiguousarray(gamma, dtype=npdt)
+    if xs[0].size != rows * hidden or gamma.size != hidden:
+        raise ValueError("oracle: shapes do not match rows x hidden")
+    P = len(xs)
+    ys = [np.empty(rows * hidden, npdt) for _ in range(P)]
+    _rc(_load().orc_all_reduce_rmsnorm(_ptrs(xs), _ptrs(ys), P, rows, hidden, gamma.ctypes.data,
+                                       float(eps), code), "all_reduce_rmsnorm")
     return ys
 
 

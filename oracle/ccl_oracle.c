@@ -34,6 +34,7 @@
  * Every function returns 0 on success and a negative value on bad input.
  * Style: scalar loops, no SIMD intrinsics, no threads, no fast-math.
  */
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -259,6 +260,61 @@ int orc_broadcast(const void *send, void *const *recv, int P, size_t count, int 
     for (int q = 0; q < P; ++q)
         for (size_t i = 0; i < count; ++i)
             memcpy((char *)recv[q] + i * s, (const char *)send + i * s, s);
+    return 0;
+}
+
+/* One element of a float dtype as fp32 (exact). */
+static float load_as_f32(const void *base, size_t i, int dtype) {
+    if (dtype == ORC_F32) {
+        float v;
+        memcpy(&v, (const char *)base + i * 4, 4);
+        return v;
+    }
+    uint16_t h;
+    memcpy(&h, (const char *)base + i * 2, 2);
+    return dtype == ORC_BF16 ? orc_bf16_widen(h) : orc_f16_widen(h);
+}
+
+static void store_from_f32(void *base, size_t i, int dtype, float v) {
+    if (dtype == ORC_F32) {
+        memcpy((char *)base + i * 4, &v, 4);
+    } else {
+        uint16_t h = dtype == ORC_BF16 ? orc_bf16_narrow(v) : orc_f16_narrow(v);
+        memcpy((char *)base + i * 2, &h, 2);
+    }
+}
+
+/*
+ * All-reduce with RMSNorm fused between its two halves ([roadmap], the Device
+ * API example that puts a Transformer RMSNorm between reduce-scatter and
+ * all-gather in one kernel).  The tensor is rows x hidden on every rank.  Per
+ * row t: s[h] = the rank-order fold of the P inputs, rounded to the dtype (the
+ * value a reduce-scatter would hand over); then, in double precision,
+ * inv = 1 / sqrt(mean_h s[h]^2 + eps) and y[h] = s[h] * inv * gamma[h],
+ * rounded to fp32 and then to the dtype; every output q receives y.
+ */
+int orc_all_reduce_rmsnorm(const void *const *send, void *const *recv, int P, size_t rows,
+                           size_t hidden, const void *gamma, double eps, int dtype) {
+    if (check_common(send, P, dtype, ORC_SUM) || !recv || !gamma || dtype == ORC_I32) return -1;
+    if (hidden == 0) return rows == 0 ? 0 : -1;
+    char tmp[8];
+    double ss;
+    for (size_t t = 0; t < rows; ++t) {
+        ss = 0.0;
+        for (size_t h = 0; h < hidden; ++h) {
+            fold_element(send, P, dtype, ORC_SUM, t * hidden + h, tmp);
+            double v = (double)load_as_f32(tmp, 0, dtype);
+            ss += v * v;
+        }
+        const double inv = 1.0 / sqrt(ss / (double)hidden + eps);
+        for (size_t h = 0; h < hidden; ++h) {
+            fold_element(send, P, dtype, ORC_SUM, t * hidden + h, tmp);
+            const double v = (double)load_as_f32(tmp, 0, dtype);
+            const double g = (double)load_as_f32(gamma, h, dtype);
+            const float y = (float)(v * inv * g);
+            for (int q = 0; q < P; ++q) store_from_f32(recv[q], t * hidden + h, dtype, y);
+        }
+    }
     return 0;
 }
 

@@ -84,3 +84,31 @@ class DevBuf:
 
 def upload_all(arrays, device, offset: int = 0):
     return [DevBuf(a.nbytes, device, offset).upload(a) for a in arrays]
+
+
+def assert_rmsnorm_parity(got: np.ndarray, want: np.ndarray, dtype: str, hidden: int,
+                          what: str = "") -> int:
+    """The fused all-reduce + RMSNorm bar.  The kernel sums squares in fp32 in
+    its own order while the oracle works in fp64, so the fp32 result may
+    differ by (hidden/2 + 4) * 2^-24 relative (recursive-summation bound on
+    the sum of squares, halved by the square root, plus the final products);
+    that is below one bf16 or fp16 ulp, so those must be within 1 ulp."""
+    half = dtype in ("bf16", "f16")
+    gb = got.view(np.uint16 if half else np.uint32)
+    wb = want.view(np.uint16 if half else np.uint32)
+    neq = gb != wb
+    if not np.any(neq):
+        return 0
+    if half:
+        bad = neq & (np.abs(_ordinal_bf16(gb) - _ordinal_bf16(wb)) > 1)
+    else:
+        g = got.astype(np.float64)
+        w = want.astype(np.float64)
+        tol = (hidden / 2 + 4) * 2.0 ** -24 * np.abs(w) + 2.0 ** -126
+        bad = neq & ~(np.abs(g - w) <= tol)
+    nbad = int(np.count_nonzero(bad))
+    if nbad:
+        i = int(np.argmax(bad))
+        raise AssertionError(f"{what}: {nbad} elements outside tolerance (first at {i}: "
+                             f"{got[i]!r} vs {want[i]!r})")
+    return int(np.count_nonzero(neq))

@@ -1,0 +1,125 @@
+"""GPU parity of the all-reduce with RMSNorm fused between its halves."""
+from __future__ import annotations
+
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from _parity import DevBuf, assert_rmsnorm_parity, upload_all
+from collective_communication_plane_amd import ccl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NP = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16}
+ESZ = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    torch.cuda.synchronize()
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def run(xs, rows, hidden, gamma, eps, dtype, in_place=False, cfg=None):
+    P = len(xs)
+    dx = upload_all(xs, DEV)
+    dg = DevBuf(gamma.nbytes, DEV).upload(gamma)
+    dy = dx if in_place else [DevBuf(rows * hidden * ESZ[dtype], DEV) for _ in range(P)]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm([b.ptr for b in dx], [b.ptr for b in dy], P, rows,
+                                         hidden, dg.ptr, eps, ccl.DTYPES[dtype],
+                                         torch.cuda.current_stream(), cfg), "ar_rmsnorm")
+    torch.cuda.synchronize()
+    for b in dx + dy + [dg]:
+        assert b.guards_intact()
+    return [b.download(NP[dtype]) for b in dy]
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("hidden", [64, 1024, 7168, 8192])
+def test_matches_oracle(P, dtype, hidden):
+    if dtype == "f32" and hidden > 8192:
+        pytest.skip("fp32 rows are limited to 8192 elements")
+    rows, eps = 19, 1e-6
+    xs = si.rank_buffers(P, rows * hidden, dtype, "normal", seed=P + hidden)
+    gamma = si.rank_buffers(1, hidden, dtype, "uniform", seed=7)[0]
+    got = run(xs, rows, hidden, gamma, eps, dtype)
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, eps, dtype)
+    for q in range(P):
+        assert_rmsnorm_parity(got[q], want[q], dtype, hidden, f"P={P} {dtype} H={hidden}")
+        np.testing.assert_array_equal(got[q], got[0])
+
+
+def test_bf16_hidden_16384_and_in_place():
+    P, rows, hidden = 4, 9, 16384
+    xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=3)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=4)[0]
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, 1e-5, "bf16")
+    got = run(xs, rows, hidden, gamma, 1e-5, "bf16", in_place=True)
+    for q in range(P):
+        assert_rmsnorm_parity(got[q], want[q], "bf16", hidden, "in place")
+
+
+@pytest.mark.parametrize("cfg", [dict(workgroups=1), dict(workgroups=7), dict(occupancy=1),
+                                 dict(occupancy=32), dict(nontemporal=4)])
+def test_launch_config_does_not_change_results(cfg):
+    P, rows, hidden = 8, 40, 4096
+    xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=9)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=10)[0]
+    base = run(xs, rows, hidden, gamma, 1e-6, "bf16")
+    got = run(xs, rows, hidden, gamma, 1e-6, "bf16", cfg=ccl.LaunchConfig(**cfg))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], base[q])
+
+
+def test_rejections():
+    P, rows, hidden = 2, 4, 64
+    bufs = [DevBuf(rows * hidden * 2, DEV) for _ in range(2 * P)]
+    g = DevBuf(hidden * 2, DEV)
+    send, recv = [b.ptr for b in bufs[:P]], [b.ptr for b in bufs[P:]]
+    st = torch.cuda.current_stream()
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, 60, g.ptr, 1e-6, ccl.CCL_BFLOAT16,
+                                      st) == ccl.CCL_ERR_UNSUPPORTED  # 120-byte rows
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, 32768, g.ptr, 1e-6, ccl.CCL_BFLOAT16,
+                                      st) == ccl.CCL_ERR_UNSUPPORTED  # row too long
+    assert ccl.ccl_all_reduce_rmsnorm([send[0] + 2, send[1]], recv, P, rows, hidden, g.ptr, 1e-6,
+                                      ccl.CCL_BFLOAT16, st) == ccl.CCL_ERR_UNSUPPORTED
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, hidden, g.ptr, -1.0, ccl.CCL_BFLOAT16,
+                                      st) == ccl.CCL_ERR_INVALID_ARG
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, hidden, g.ptr, 1e-6, ccl.CCL_INT32,
+                                      st) == ccl.CCL_ERR_INVALID_ARG
+    assert ccl.ccl_all_reduce_rmsnorm(send, [recv[0], recv[0] + 16], P, rows, hidden, g.ptr, 1e-6,
+                                      ccl.CCL_BFLOAT16, st) == ccl.CCL_ERR_ALIASING
+    torch.cuda.synchronize()
+    for b in bufs[P:]:
+        assert (b.base == b.fill).all().item()
+
+
+def test_full_size_sampled_rows():
+    """P=8, 16384 tokens x 8192 hidden bf16 (256 MiB per rank): exact replica
+    identity on the GPU and sampled rows against the oracle."""
+    P, rows, hidden = 8, 16384, 8192
+    dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=DEV)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
+    dg = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
+    dy = [torch.empty_like(t) for t in dx]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16,
+                                         torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    for q in range(1, P):
+        assert torch.equal(dy[q].view(torch.int16), dy[0].view(torch.int16))
+    sample = si.sample_indices(rows, 64, seed=2).astype(np.int64)
+    xs = [t.view(rows, hidden)[torch.from_numpy(sample).to(DEV)].view(torch.int16).cpu().numpy()
+          .view(np.uint16).ravel() for t in dx]
+    want = oracle.all_reduce_rmsnorm(xs, sample.size, hidden, gamma, 1e-6, "bf16")[0]
+    got = dy[0].view(rows, hidden)[torch.from_numpy(sample).to(DEV)].view(torch.int16).cpu().numpy()
+    assert_rmsnorm_parity(got.view(np.uint16).ravel(), want, "bf16", hidden, "full size")

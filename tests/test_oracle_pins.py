@@ -460,3 +460,42 @@ def test_uneven_reshard_round_trip():
     mid = oracle.reshard((11, 7), a, b, local_blocks(t, a))
     back = oracle.reshard((11, 7), b, c, mid)
     np.testing.assert_array_equal(back[0], t.ravel())
+
+
+# ------------------------------------------------- all-reduce + RMSNorm
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_allreduce_rmsnorm_equals_torch_rms_norm_of_the_reduce(P, dtype):
+    rows, hidden, eps = 6, 96, 1e-6
+    xs = si.rank_buffers(P, rows * hidden, dtype, "normal", seed=P)
+    gamma = si.rank_buffers(1, hidden, dtype, "uniform", seed=99)[0]
+    ys = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, eps, dtype)
+    s = oracle.reduce(xs, dtype, "sum")  # the reduce-scatter's rounded values
+
+    def widen(a):
+        if dtype == "bf16":
+            return si.bf16_bits_to_f32(a).astype(np.float64)
+        if dtype == "f16":
+            return a.view(np.float16).astype(np.float64)
+        return a.astype(np.float64)
+
+    S = torch.from_numpy(widen(s).reshape(rows, hidden))
+    G = torch.from_numpy(widen(gamma))
+    ref = torch.nn.functional.rms_norm(S, (hidden,), weight=G, eps=eps).numpy().astype(np.float32)
+    if dtype == "bf16":
+        want = si.to_bf16_bits(ref.ravel())
+    elif dtype == "f16":
+        want = ref.ravel().astype(np.float16).view(np.uint16)
+    else:
+        want = ref.ravel()
+    for y in ys:
+        np.testing.assert_array_equal(y, want)
+
+
+def test_allreduce_rmsnorm_rows_are_unit_rms_with_unit_gamma():
+    rows, hidden = 4, 512
+    xs = si.rank_buffers(3, rows * hidden, "f32", "normal", seed=5)
+    y = oracle.all_reduce_rmsnorm(xs, rows, hidden, np.ones(hidden, np.float32), 0.0, "f32")[0]
+    rms = np.sqrt(np.mean(y.reshape(rows, hidden).astype(np.float64) ** 2, axis=1))
+    np.testing.assert_allclose(rms, 1.0, rtol=1e-6)
