@@ -17,8 +17,9 @@ Besides the headline value the line carries:
                 (single thread);
   rows          the other data-plane workloads (reduce-scatter bf16 and int32,
                 all-gather, the all-reduce through the LDS pipeline, the
-                all-reduce with fused RMSNorm, the two weight reshards), each
-                timed the same way after a warmup of at least half a second.
+                all-reduce with fused RMSNorm, the two weight reshards and the
+                first one quantized to FP8 while staged), each timed the same way
+                after a warmup of at least half a second.
 
 Other modes:
   --sweep       the launch-configuration sweep (chunk bytes, stages, unroll,
@@ -217,9 +218,21 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
         ccl.check(st, "reshard_plan")
         ms = timed(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream)), steps,
                    warmup, stream, warm_s)
-        ccl.check(ccl.ccl_plan_destroy(plan))
         record(name, tensor_bytes * (1 + rho), ms,
                f"reshard {list(shape)} bf16 {src} -> {dst}")
+        if name == "reshard_weight":
+            # the same reshard, quantized to FP8 E4M3 with 128-element scales while staged
+            n_local = dbytes // 2
+            codes = [torch.empty(n_local, dtype=torch.uint8, device=dev) for _ in range(ndst)]
+            scales = [torch.empty(n_local // 128, dtype=torch.float32, device=dev)
+                      for _ in range(ndst)]
+            ms = timed(lambda: ccl.check(ccl.ccl_reshard_copy_fp8(plan, dsrc, codes, scales, stream)),
+                       steps, warmup, stream, warm_s)
+            record("reshard_weight_fp8", tensor_bytes + ndst * (n_local + n_local // 128 * 4), ms,
+                   f"reshard {list(shape)} bf16 {src} -> {dst}, stored as FP8 E4M3 + fp32 "
+                   "scale per 128 elements")
+            del codes, scales
+        ccl.check(ccl.ccl_plan_destroy(plan))
         del dsrc, ddst
         torch.cuda.empty_cache()
     return out

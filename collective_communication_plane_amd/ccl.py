@@ -87,7 +87,7 @@ EXPORTS = [
     "ccl_all_reduce", "ccl_reduce_scatter", "ccl_all_gather", "ccl_reduce", "ccl_broadcast",
     "ccl_all_reduce_rmsnorm",
     "ccl_reshard_plan",
-    "ccl_reshard_copy", "ccl_plan_destroy", "ccl_plan_num_intervals", "ccl_plan_get_interval",
+    "ccl_reshard_copy", "ccl_reshard_copy_fp8", "ccl_plan_destroy", "ccl_plan_num_intervals", "ccl_plan_get_interval",
     "ccl_plan_local_bytes", "ccl_plan_num_dst_shards", "ccl_plan_shard_replicas",
     "ccl_get_error_string", "ccl_version",
 ]
@@ -119,6 +119,7 @@ def _load():
                                      ctypes.POINTER(Placement), ctypes.POINTER(Mesh),
                                      ctypes.POINTER(Placement), ctypes.POINTER(vp)]
     lib.ccl_reshard_copy.argtypes = [vp, pp, pp, vp, pcfg]
+    lib.ccl_reshard_copy_fp8.argtypes = [vp, pp, pp, pp, vp, pcfg]
     lib.ccl_plan_destroy.argtypes = [vp]
     lib.ccl_plan_num_intervals.argtypes = [vp, ctypes.POINTER(ctypes.c_uint64)]
     lib.ccl_plan_get_interval.argtypes = [vp, ctypes.c_uint64, ctypes.POINTER(Interval)]
@@ -258,6 +259,11 @@ def ccl_reshard_plan(tensor: TensorDesc, src_mesh: Mesh, src_placements, dst_mes
 def ccl_reshard_copy(plan, src_bufs, dst_bufs, stream=None, cfg=None) -> int:
     s, d = _ptr_array(src_bufs), _ptr_array(dst_bufs)
     return _load().ccl_reshard_copy(plan, _pp(s), _pp(d), _stream(stream), _cfg(cfg))
+
+
+def ccl_reshard_copy_fp8(plan, src_bufs, dst_codes, dst_scales, stream=None, cfg=None) -> int:
+    s, c, f = _ptr_array(src_bufs), _ptr_array(dst_codes), _ptr_array(dst_scales)
+    return _load().ccl_reshard_copy_fp8(plan, _pp(s), _pp(c), _pp(f), _stream(stream), _cfg(cfg))
 
 
 def ccl_plan_destroy(plan) -> int:

@@ -3,6 +3,7 @@
 // to the kernels in ccl_collectives.hip / ccl_reshard.hip.
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "ccl_internal.h"
 
@@ -312,6 +313,43 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
   }
   if (p->intervals.empty()) return CCL_OK;
   return ccl::reshard_launch(p, src_bufs, dst_bufs, l, (hipStream_t)stream);
+}
+
+ccl_status_t ccl_reshard_copy_fp8(const ccl_plan_t *plan, const void *const *src_bufs,
+                                  void *const *dst_codes, float *const *dst_scales, void *stream,
+                                  const ccl_launch_config_t *cfg) {
+  ccl::Launch l;
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD, 0, &l);
+  if (st) return st;
+  if (!plan || !src_bufs || !dst_codes || !dst_scales) return CCL_ERR_INVALID_ARG;
+  ccl_plan *p = const_cast<ccl_plan *>(plan);
+  if (p->dtype != CCL_FLOAT32 && p->dtype != CCL_BFLOAT16 && p->dtype != CCL_FLOAT16)
+    return CCL_ERR_UNSUPPORTED;
+  if (!p->fp8_blocks_ok || !p->offsets_aligned16) return CCL_ERR_UNSUPPORTED;
+  const uint64_t esz = (uint64_t)p->elem_size;
+  std::vector<Range> outs;
+  for (int i = 0; i < p->n_src; ++i)
+    if (p->src_local_bytes[i] && (!src_bufs[i] || (uintptr_t)src_bufs[i] % ccl::kVecBytes))
+      return src_bufs[i] ? CCL_ERR_UNSUPPORTED : CCL_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_dst; ++i) {
+    const uint64_t n = p->dst_local_bytes[i] / esz;
+    if (!n) continue;
+    if (!dst_codes[i] || !dst_scales[i]) return CCL_ERR_INVALID_ARG;
+    if ((uintptr_t)dst_codes[i] % ccl::kVecBytes) return CCL_ERR_UNSUPPORTED;
+    if ((uintptr_t)dst_scales[i] % sizeof(float)) return CCL_ERR_INVALID_ARG;
+    outs.push_back({(uintptr_t)dst_codes[i], (uintptr_t)dst_codes[i] + n});
+    outs.push_back({(uintptr_t)dst_scales[i], (uintptr_t)dst_scales[i] + (n + 127) / 128 * 4});
+  }
+  for (size_t a = 0; a < outs.size(); ++a) {
+    for (size_t b = a + 1; b < outs.size(); ++b)
+      if (overlap(outs[a], outs[b])) return CCL_ERR_ALIASING;
+    for (int s = 0; s < p->n_src; ++s) {
+      Range rs{(uintptr_t)src_bufs[s], (uintptr_t)src_bufs[s] + p->src_local_bytes[s]};
+      if (rs.lo != rs.hi && overlap(outs[a], rs)) return CCL_ERR_ALIASING;
+    }
+  }
+  if (p->intervals.empty()) return CCL_OK;
+  return ccl::reshard_fp8_launch(p, src_bufs, dst_codes, dst_scales, l, (hipStream_t)stream);
 }
 
 }  // extern "C"

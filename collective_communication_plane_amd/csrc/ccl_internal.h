@@ -136,6 +136,7 @@ struct DevicePlanCache {
 
 struct ccl_plan {
   int32_t elem_size;
+  int32_t dtype;
   int32_t src_start, dst_start;
   int32_t n_src, n_dst;                 // ranks in each mesh
   int32_t n_dst_shards;
@@ -144,6 +145,7 @@ struct ccl_plan {
   std::vector<std::vector<int32_t>> replicas;  // per dst shard: local dst indices, ascending
   std::vector<ccl::PlanInterval> intervals;
   bool offsets_aligned16 = true;         // every interval offset is a multiple of 16
+  bool fp8_blocks_ok = true;             // every 128-element destination block lies in one interval
   // Device-side state, created on first use.
   std::mutex mu;
   std::vector<ccl::DevicePlanCache> dev;
@@ -152,5 +154,7 @@ struct ccl_plan {
 namespace ccl {
 ccl_status_t reshard_launch(ccl_plan *plan, const void *const *src, void *const *dst,
                             const Launch &l, hipStream_t stream);
+ccl_status_t reshard_fp8_launch(ccl_plan *plan, const void *const *src, void *const *codes,
+                                float *const *scales, const Launch &l, hipStream_t stream);
 void reshard_release(ccl_plan *plan);
 }  // namespace ccl

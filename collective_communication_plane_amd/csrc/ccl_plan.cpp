@@ -130,6 +130,7 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
   ccl_plan *p = new (std::nothrow) ccl_plan();
   if (!p) return CCL_ERR_NOMEM;
   p->elem_size = esz;
+  p->dtype = tensor->dtype;
   p->src_start = S.start;
   p->dst_start = D.start;
   p->n_src = S.size;
@@ -214,8 +215,13 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
         p->intervals[j].leader = D.start + rep[(j - first) % rep.size()];
     }
   }
-  for (const auto &iv : p->intervals)
+  const uint64_t block_bytes = 128 * (uint64_t)esz;
+  for (const auto &iv : p->intervals) {
     if (iv.src_off % 16 || iv.dst_off % 16) p->offsets_aligned16 = false;
+    const uint64_t end = iv.dst_off + iv.len;
+    const uint64_t local = p->dst_local_bytes[p->replicas[iv.dst_shard][0]];
+    if (iv.dst_off % block_bytes || (end % block_bytes && end != local)) p->fp8_blocks_ok = false;
+  }
   *plan_out = p;
   return CCL_OK;
 }

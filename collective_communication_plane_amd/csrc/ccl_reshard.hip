@@ -120,6 +120,117 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
   }
 }
 
+// ------------------------------------------------ fp8 staging quantization
+//
+// The digest's M2N section lists quantizing weights on the fly inside the
+// staging kernel as future work, with no format.  This library's format: OCP
+// FP8 E4M3 (bias 7, largest finite 448, no infinities) with one fp32 scale
+// per block of 128 consecutive elements of each destination's local buffer;
+// scale = amax / 448 (1 for an all-zero block), code = round-to-nearest-even
+// of x / scale, saturated at +-448.  The plan must place every block inside
+// one interval (checked on the host), so a group of lanes owns one block:
+// its lanes read the block's 16-byte vectors once, agree on amax through
+// shuffles, and store codes and scale to every replica.
+
+constexpr int kFp8Block = 128;
+
+struct ReshardFp8Args {
+  const char *src[CCL_MAX_MESH_RANKS];
+  char *codes[CCL_MAX_MESH_RANKS];
+  float *scales[CCL_MAX_MESH_RANKS];
+  const DevInterval *iv;
+  const int32_t *rep;
+  const uint32_t *chunk_iv;
+  uint64_t total_chunks;
+  uint64_t chunk_bytes;  // source bytes per chunk, a multiple of the block's bytes
+  int n_iv;
+  int rho;
+  int flags;
+};
+
+// fp32 -> E4M3 code, round to nearest even, saturating; |y| must not be NaN.
+__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (!(a < 448.0f)) return sign | 0x7eu;
+  if (a < 0.015625f) {  // below 2^-6: a multiple of 2^-9, exact scaling then RNE
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  const uint32_t ua = __float_as_uint(a);
+  const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);  // keep 3 mantissa bits
+  const uint32_t e = (r >> 23) - 127u + 7u;
+  return sign | (e << 3) | ((r >> 20) & 7u);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a) {
+  constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
+  constexpr int EPL = kVecBytes / esz;             // elements per lane
+  constexpr int LPB = kFp8Block / EPL;             // lanes per block (16 or 32)
+  const bool ntl = a.flags & 1;
+  for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
+    const int i = a.chunk_iv ? (int)a.chunk_iv[c] : find_interval(a.iv, a.n_iv, c);
+    const DevInterval iv = a.iv[i];
+    const uint64_t off = (c - iv.first_chunk) * a.chunk_bytes;
+    const uint64_t bytes = min(a.chunk_bytes, iv.len - off);
+    const char *src = a.src[iv.src_local] + iv.src_off + off;
+    const int32_t *rep = a.rep + (uint64_t)iv.dst_shard * a.rho;
+    const uint64_t elem0 = (iv.dst_off + off) / esz;  // first destination element, block-aligned
+    const uint64_t nvec = (bytes + kVecBytes - 1) / kVecBytes;
+    // whole groups iterate together so shuffles see every lane of a block
+    for (uint64_t v0 = 0; v0 < nvec; v0 += kThreads) {
+      const uint64_t v = v0 + threadIdx.x;
+      const bool live = v * kVecBytes < bytes;
+      float x[EPL];
+      float amax = 0.f;
+      if (live) {
+        const u32x4 w = ntl ? ld_nt(src + v * kVecBytes) : ld_plain(src + v * kVecBytes);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (DT == CCL_FLOAT32) {
+            x[k] = __uint_as_float(w[k]);
+          } else if constexpr (DT == CCL_BFLOAT16) {
+            x[2 * k] = bf16_lo(w[k]);
+            x[2 * k + 1] = bf16_hi(w[k]);
+          } else {
+            x[2 * k] = f16_lo(w[k]);
+            x[2 * k + 1] = f16_hi(w[k]);
+          }
+        }
+        // a short last block: elements past the interval do not count
+        const uint64_t valid = min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          if ((uint64_t)e < valid) amax = fmaxf(amax, fabsf(x[e]));
+      }
+#pragma unroll
+      for (int m = LPB / 2; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+      if (!live) continue;
+      const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+      const uint64_t valid = min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz);
+      uint32_t q[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) q[e] = e4m3_rne_sat(x[e] / scale);
+      const uint64_t elem = elem0 + v * EPL;
+      for (int j = 0; j < a.rho; ++j) {
+        char *d = a.codes[rep[j]] + elem;
+        if (valid == (uint64_t)EPL) {
+          if constexpr (EPL == 8) {
+            uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+            uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+            *(uint2 *)d = make_uint2(lo, hi);
+          } else {
+            *(uint32_t *)d = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          }
+        } else {
+          for (uint64_t e = 0; e < valid; ++e) d[e] = (char)q[e];
+        }
+        if ((threadIdx.x % LPB) == 0) a.scales[rep[j]][elem / kFp8Block] = scale;
+      }
+    }
+  }
+}
+
 // Build (or find) the device copy of the plan for this device and chunk size.
 ccl_status_t device_table(ccl_plan *p, int dev, uint64_t chunk_bytes, DevicePlanCache *out) {
   std::lock_guard<std::mutex> lock(p->mu);
@@ -205,6 +316,48 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
   hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kThreads),
                      occupancy_lds(l.occupancy, 0), stream, a);
+  return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+}
+
+ccl_status_t reshard_fp8_launch(ccl_plan *p, const void *const *src, void *const *codes,
+                                float *const *scales, const Launch &l, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
+  const uint64_t block_bytes = (uint64_t)kFp8Block * p->elem_size;
+  // chunks hold whole blocks
+  const uint64_t chunk = std::max<uint64_t>(block_bytes, l.chunk_bytes / block_bytes * block_bytes);
+  DevicePlanCache e;
+  ccl_status_t st = device_table(p, dev, chunk, &e);
+  if (st) return st;
+  ReshardFp8Args a{};
+  for (int i = 0; i < p->n_src; ++i) a.src[i] = (const char *)src[i];
+  for (int i = 0; i < p->n_dst; ++i) {
+    a.codes[i] = (char *)codes[i];
+    a.scales[i] = scales[i];
+  }
+  a.iv = (const DevInterval *)e.table;
+  a.rep = (const int32_t *)((const char *)e.table + e.rep_offset);
+  a.chunk_iv = e.chunk_iv_offset ? (const uint32_t *)((const char *)e.table + e.chunk_iv_offset)
+                                  : nullptr;
+  a.total_chunks = e.total_chunks;
+  a.chunk_bytes = chunk;
+  a.n_iv = (int)p->intervals.size();
+  a.rho = p->n_dst / p->n_dst_shards;
+  a.flags = l.nt_load ? 1 : 0;
+  uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
+  grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
+  const size_t lds = occupancy_lds(l.occupancy, 0);
+  switch (p->dtype) {
+    case CCL_FLOAT32:
+      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_FLOAT32>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+      break;
+    case CCL_BFLOAT16:
+      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_BFLOAT16>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+      break;
+    default:
+      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_FLOAT16>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+      break;
+  }
   return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
 

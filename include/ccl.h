@@ -302,6 +302,30 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
                               void *const *dst_bufs, void *stream,
                               const ccl_launch_config_t *cfg);
 
+/*
+ * Execute a plan with on-the-fly quantization in the staging pass (the
+ * digest's M2N section lists quantizing weights inside the staging kernel as
+ * future work and fixes no format; this is the format chosen here).  Every
+ * destination buffer is written as OCP FP8 E4M3 codes (1 byte per element,
+ * bias 7, largest finite 448) plus one fp32 scale per block of 128
+ * consecutive elements of its local buffer: scale = amax / 448 in fp32 (1 for
+ * an all-zero block), code = round-to-nearest-even of x / scale in fp32,
+ * saturated to +-448.  Dequantize as code_value * scale.
+ *
+ *   src_bufs    as for ccl_reshard_copy (element type: fp32, bf16 or fp16).
+ *   dst_codes   one pointer per destination-mesh rank, local-element-count
+ *               bytes, 16-byte aligned.
+ *   dst_scales  one pointer per destination-mesh rank, ceil(local elements /
+ *               128) floats.
+ * Returns CCL_ERR_UNSUPPORTED when the plan would split a 128-element
+ * destination block across intervals or any interval offset is not 16-byte
+ * aligned, and for an int32 plan.  Overlaps among the outputs or with a
+ * source give CCL_ERR_ALIASING.
+ */
+ccl_status_t ccl_reshard_copy_fp8(const ccl_plan_t *plan, const void *const *src_bufs,
+                                  void *const *dst_codes, float *const *dst_scales, void *stream,
+                                  const ccl_launch_config_t *cfg);
+
 /* Release a plan and its device table.  Work that uses it must be complete. */
 ccl_status_t ccl_plan_destroy(ccl_plan_t *plan);
 

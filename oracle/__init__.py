@@ -63,6 +63,12 @@ def _load():
         lib.orc_reduce.argtypes = [pp, vp, i32, sz, i32, i32]
         lib.orc_broadcast.argtypes = [vp, pp, i32, sz, i32]
         lib.orc_all_reduce_rmsnorm.argtypes = [pp, pp, i32, sz, sz, vp, ctypes.c_double, i32]
+        lib.orc_quantize_e4m3.argtypes = [vp, i32, sz, sz, vp, vp]
+        lib.orc_quantize_e4m3.restype = i32
+        lib.orc_e4m3_value.argtypes = [ctypes.c_uint]
+        lib.orc_e4m3_value.restype = ctypes.c_double
+        lib.orc_e4m3_nearest_sat.argtypes = [ctypes.c_float]
+        lib.orc_e4m3_nearest_sat.restype = ctypes.c_uint
         lay = [i32, p64, i64, pint, pint]
         lib.orc_reshard.argtypes = [i32, p64, i32] + lay + lay + [pp, pp]
         lib.orc_reshard_at.argtypes = [i32, p64, i32] + lay + lay + [pp, i64, pu64, sz, vp]
@@ -255,6 +261,30 @@ def narrow_bf16(x: float) -> int:
 
 def widen_bf16(h: int) -> float:
     return float(_load().orc_widen_bf16(int(h)))
+
+
+def quantize_e4m3(x, dtype: str, block: int = 128):
+    """Blockwise FP8 E4M3 quantization: (codes uint8, scales float32)."""
+    code, npdt, (x,) = _check_bufs([x], dtype)
+    codes = np.empty(x.size, np.uint8)
+    scales = np.empty((x.size + block - 1) // block, np.float32)
+    _rc(_load().orc_quantize_e4m3(x.ctypes.data, code, x.size, block, codes.ctypes.data,
+                                  scales.ctypes.data), "quantize_e4m3")
+    return codes, scales
+
+
+def reshard_fp8(shape, src_layout, dst_layout, src_bufs, dtype: str, block: int = 128):
+    """Reshard, then quantize every destination buffer blockwise to E4M3."""
+    dst = reshard(shape, src_layout, dst_layout, src_bufs)
+    return [quantize_e4m3(d, dtype, block) for d in dst]
+
+
+def e4m3_value(code: int) -> float:
+    return float(_load().orc_e4m3_value(int(code)))
+
+
+def e4m3_nearest_sat(y: float) -> int:
+    return int(_load().orc_e4m3_nearest_sat(float(y)))
 
 
 def narrow_f16(x: float) -> int:

@@ -545,6 +545,68 @@ int orc_reshard_at(int ndim, const int64_t *shape, int elem_size,
     return 0;
 }
 
+/* ------------------------------------------------- fp8 staging quantization */
+
+/*
+ * OCP FP8 E4M3 ("e4m3fn": 1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities, S.1111.111 is NaN, largest finite 448): the value of a
+ * code, straight from that definition.
+ */
+static double e4m3_value(unsigned code) {
+    const unsigned e = (code >> 3) & 15u, m = code & 7u;
+    double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, (int)e - 7);
+    return (code & 0x80u) ? -v : v;
+}
+
+/*
+ * Nearest E4M3 code to y, ties to the code with an even mantissa, magnitudes
+ * above 448 saturated to 448 (a brute-force search over the 127 finite
+ * non-negative codes).  The sign of y (including -0) is kept.
+ */
+static unsigned e4m3_nearest_sat(float y) {
+    const double a = fabs((double)y);
+    const unsigned sign = signbit(y) ? 0x80u : 0u;
+    if (a >= 448.0) return sign | 0x7eu;
+    unsigned best = 0;
+    double best_d = a;
+    for (unsigned c = 1; c < 0x7f; ++c) {
+        const double d = fabs(e4m3_value(c) - a);
+        if (d < best_d || (d == best_d && (c & 1u) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | best;
+}
+
+/*
+ * Quantize n elements in blocks of `block`: per block, amax = max |x| (fp32),
+ * scale = amax / 448 in fp32 (1 when amax is 0), code = nearest E4M3 to
+ * x / scale in fp32.  The M2N part of the digest (lqnn.cn news 207677) s1.5
+ * names quantizing weights on the fly inside the staging kernel as future
+ * work without fixing a format; this is the format this library picks.
+ */
+int orc_quantize_e4m3(const void *x, int dtype, size_t n, size_t block, uint8_t *codes,
+                      float *scales) {
+    if (!x || dtype == ORC_I32 || dtype_size(dtype) == 0 || block == 0 || (n && (!codes || !scales)))
+        return -1;
+    for (size_t b0 = 0; b0 < n; b0 += block) {
+        const size_t b1 = b0 + block < n ? b0 + block : n;
+        float amax = 0.f;
+        for (size_t i = b0; i < b1; ++i) {
+            const float v = fabsf(load_as_f32(x, i, dtype));
+            if (v > amax) amax = v;
+        }
+        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        scales[b0 / block] = scale;
+        for (size_t i = b0; i < b1; ++i) codes[i] = (uint8_t)e4m3_nearest_sat(load_as_f32(x, i, dtype) / scale);
+    }
+    return 0;
+}
+
+double orc_e4m3_value(unsigned code) { return e4m3_value(code); }
+unsigned orc_e4m3_nearest_sat(float y) { return e4m3_nearest_sat(y); }
+
 /* Number of elements the l-th rank of a layout holds (its box volume). */
 int64_t orc_local_numel(int ndim, const int64_t *shape, int m_ndims, const int64_t *m_dims,
                         const int *kind, const int *sdim, int64_t l) {

@@ -203,3 +203,82 @@ def test_example_b_two_pipeline_stages():
                                           oracle.reshard(shape, src, dst, halves)[0])
     finally:
         ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+# ------------------------------------------------ fp8 staging quantization
+
+FP8_CASES = [
+    ((8, 256), ([1, 4], 0, ["R", ("S", 0)]), ([2, 2], 4, ["R", ("S", 0)])),   # Example A layout
+    ((64, 2048, 128), ([8], 0, [("S", 0)]), ([4], 8, [("S", 1)])),             # MoE-like
+    ((1024, 384), ([4], 0, [("S", 0)]), ([1], 4, ["R"])),                      # gather to one
+    ((3, 1000), ([1], 0, ["R"]), ([3], 1, [("S", 0)])),                        # 1000: short last block
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_CASES)))
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_reshard_fp8_matches_oracle(case, dtype):
+    shape, src, dst = FP8_CASES[case]
+    G = si.tensor(shape, dtype, "w002", seed=case + 20)
+    src_bufs = local_blocks(G, src)
+    want = oracle.reshard_fp8(shape, src, dst, src_bufs, dtype)
+    plan = make_plan(shape, ccl.DTYPES[dtype], src, dst)
+    try:
+        dsrc = upload_all(src_bufs, DEV)
+        codes = [DevBuf(w[0].size, DEV) for w in want]
+        scales = [DevBuf(w[1].nbytes, DEV) for w in want]
+        ccl.check(ccl.ccl_reshard_copy_fp8(plan, [b.ptr for b in dsrc], [b.ptr for b in codes],
+                                           [b.ptr for b in scales], torch.cuda.current_stream()),
+                  "reshard_copy_fp8")
+        torch.cuda.synchronize()
+        for c, f, (wc, wf) in zip(codes, scales, want):
+            assert c.guards_intact() and f.guards_intact()
+            np.testing.assert_array_equal(f.download(np.float32).view(np.uint32), wf.view(np.uint32))
+            np.testing.assert_array_equal(c.download(np.uint8), wc)
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+def test_reshard_fp8_rejects_split_blocks():
+    # rows of 100 elements: the MoE-like column split cuts 128-element blocks
+    plan = make_plan((16, 100), ccl.CCL_BFLOAT16, ([2], 0, [("S", 0)]), ([2], 2, [("S", 1)]))
+    try:
+        base = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+        p = base.data_ptr()
+        st = ccl.ccl_reshard_copy_fp8(plan, [p, p + 4096], [p + 8192, p + 12288],
+                                      [p + 16384, p + 20480], torch.cuda.current_stream())
+        assert st == ccl.CCL_ERR_UNSUPPORTED
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+def test_reshard_fp8_weight_full_size_sampled():
+    """[8192, 28672] bf16, TP4 -> TP2 x DP2, quantized in the staging pass."""
+    shape = (8192, 28672)
+    src = ([1, 4], 0, ["R", ("S", 0)])
+    dst = ([2, 2], 4, ["R", ("S", 0)])
+    G = si.tensor(shape, "bf16", "w002", seed=0)
+    src_host = local_blocks(G, src)
+    del G
+    dsrc = [torch.from_numpy(b.view(np.uint8)).to(DEV) for b in src_host]
+    n = 4096 * 28672
+    codes = [torch.empty(n, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    scales = [torch.empty(n // 128, dtype=torch.float32, device=DEV) for _ in range(4)]
+    plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
+    try:
+        ccl.check(ccl.ccl_reshard_copy_fp8(plan, dsrc, codes, scales, torch.cuda.current_stream()))
+        torch.cuda.synchronize()
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+    # replicas 4/6 and 5/7 are identical
+    assert torch.equal(codes[0], codes[2]) and torch.equal(codes[1], codes[3])
+    assert torch.equal(scales[0], scales[2]) and torch.equal(scales[1], scales[3])
+    # sampled blocks against the oracle's quantization of the resharded values
+    for l in range(2):
+        blocks = si.sample_indices(n // 128, 300, seed=l + 9).astype(np.int64)
+        idx = (blocks[:, None] * 128 + np.arange(128)[None, :]).ravel()
+        vals = oracle.reshard_at(shape, src, dst, src_host, l, idx.astype(np.uint64))
+        wc, wf = oracle.quantize_e4m3(vals, "bf16")
+        it = torch.from_numpy(idx).to(DEV)
+        np.testing.assert_array_equal(codes[l][it].cpu().numpy(), wc)
+        np.testing.assert_array_equal(scales[l][torch.from_numpy(blocks).to(DEV)].cpu().numpy(), wf)

@@ -499,3 +499,48 @@ def test_allreduce_rmsnorm_rows_are_unit_rms_with_unit_gamma():
     y = oracle.all_reduce_rmsnorm(xs, rows, hidden, np.ones(hidden, np.float32), 0.0, "f32")[0]
     rms = np.sqrt(np.mean(y.reshape(rows, hidden).astype(np.float64) ** 2, axis=1))
     np.testing.assert_allclose(rms, 1.0, rtol=1e-6)
+
+
+# ------------------------------------------------ fp8 staging quantization
+
+def test_e4m3_code_values_match_torch_float8():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    np.testing.assert_array_equal(got, want)
+    assert oracle.e4m3_value(0x7E) == 448.0 and oracle.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3_rounding_matches_torch_in_range():
+    rng = np.random.default_rng(3)
+    y = (np.exp2(rng.uniform(-12, 8.8, 30000)) * rng.choice([-1, 1], 30000)).astype(np.float32)
+    y = y[np.abs(y) <= 448]
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_nearest_sat(float(v)) for v in y], np.uint8)
+    np.testing.assert_array_equal(got, want)
+
+
+@pytest.mark.parametrize("y, code", [
+    (448.0, 0x7E), (449.0, 0x7E), (1e30, 0x7E), (-500.0, 0xFE),    # saturation
+    (1.0625, 0x38), (1.1875, 0x3A),                                   # ties to even mantissa
+    (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02),                       # subnormal ties
+    (-0.0, 0x80), (0.0, 0x00),
+])
+def test_e4m3_hand_worked(y, code):
+    assert oracle.e4m3_nearest_sat(y) == code
+
+
+def test_blockwise_quantization_round_trip_error_bound():
+    x = si.rank_buffers(1, 128 * 40 + 17, "bf16", "w002", seed=8)[0]
+    codes, scales = oracle.quantize_e4m3(x, "bf16")
+    xf = si.bf16_bits_to_f32(x).astype(np.float64)
+    deq = np.array([oracle.e4m3_value(int(c)) for c in codes]) * np.repeat(scales, 128)[: x.size]
+    # each block's largest element maps to 448; E4M3 keeps 3 mantissa bits, so
+    # a value within the normal range is off by at most 2^-4 of itself, and
+    # anything in a block by at most half a subnormal step of that block
+    for b in range(scales.size):
+        sl = slice(128 * b, min(128 * (b + 1), x.size))
+        amax = np.max(np.abs(xf[sl]))
+        assert np.isclose(np.max(np.abs(deq[sl])), amax, rtol=2 ** -4)
+        err = np.abs(deq[sl] - xf[sl])
+        assert np.all(err <= np.maximum(np.abs(xf[sl]) * 2 ** -4, scales[b] * 2.0 ** -10) * 1.0001)
