@@ -3,7 +3,10 @@
 
 One step = one ccl_all_reduce call (sum, fold in fp32 in rank order, bf16 in
 and out) over 8 rank buffers of 134,217,728 bf16 each, resident in HBM before
-the timed region starts; it reads 2 GiB and writes 2 GiB.  W warmup steps run
+the timed region starts; it reads 2 GiB and writes 2 GiB.  The 8 inputs share
+one allocation at a stride of 256 MiB + 2 MiB + 4 KiB, and so do the outputs
+(see RANK_GAP; a row repeats the run with one tensor per rank buffer).  W
+warmup steps run
 untimed, then K steps are timed with HIP events on the stream the kernels are
 launched on, bracketed by device synchronizations.  Rank 0 prints one JSON
 line.
@@ -16,7 +19,8 @@ Besides the headline value the line carries:
   cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
                 (single thread);
   rows          the other data-plane workloads (reduce-scatter bf16 and int32,
-                all-gather, the all-reduce through the LDS pipeline, the
+                all-gather, the all-reduce under the allocator's placement and
+                through the LDS pipeline, the
                 all-reduce with fused RMSNorm, the two weight reshards and the
                 first one quantized to FP8 while staged), each timed the same way
                 after a warmup of at least half a second.
@@ -78,6 +82,7 @@ def read_traffic(bytes_per_launch_alg: float):
 
 
 def timed(launch, steps: int, warmup: int, stream, min_warm_s: float = 0.0):
+    """ms per launch over `steps` launches, after `warmup` untimed ones."""
     import torch
 
     for _ in range(warmup):
@@ -103,6 +108,26 @@ def up(a, dev):
     import torch
 
     return torch.from_numpy(np.ascontiguousarray(a).view(np.uint8)).to(dev)
+
+
+# Gap between consecutive simulated rank buffers in one allocation.  HBM
+# bandwidth with 2P concurrent streams depends on where the buffers start
+# relative to each other: buffers congruent modulo 2 MiB (what the caching
+# allocator hands out for equal large sizes) make the P streams contend for
+# the same DRAM banks, and an extra 2 MiB + 4 KiB between neighbours spreads
+# them.  The headline places its ranks this way; a row repeats it under the
+# allocator's own placement.
+RANK_GAP = (2 << 20) + 4096
+
+
+def rank_slab(P: int, nbytes: int, dev, gap: int = RANK_GAP):
+    """P byte views of `nbytes` each, at a stride of nbytes + gap (rounded up
+    to 256 bytes) inside one allocation; the views keep it alive."""
+    import torch
+
+    stride = (nbytes + gap + 255) // 256 * 256
+    slab = torch.empty(P * stride, dtype=torch.uint8, device=dev)
+    return [slab[r * stride:r * stride + nbytes] for r in range(P)], stride
 
 
 def cpu_baseline(seconds: float = 10.0):
@@ -169,10 +194,16 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     del dx, dy
     torch.cuda.empty_cache()
 
-    # the headline all-reduce again, through the LDS pipeline instead of VGPRs
+    # the headline all-reduce with the caching allocator's placement (one
+    # tensor per rank buffer), then through the LDS pipeline instead of VGPRs
     n = 134_217_728
     dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
     dy = [torch.empty_like(t) for t in dx]
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                                    stream)), steps, warmup, stream, warm_s)
+    record("all_reduce_bf16_allocator_placement", 2 * P * n * 2, ms,
+           "all_reduce sum, P=8 x 134,217,728 bf16, library defaults, one torch tensor per "
+           "rank buffer (the caching allocator's placement)")
     lds_cfg = ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=2)
     ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
                                                     stream, lds_cfg)), steps, warmup, stream, warm_s)
@@ -327,7 +358,11 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=500)
+    # Somewhere between the 540th and the 590th kernel launch of a process the
+    # HIP runtime holds one launch call on the host for 30-60 ms (once per
+    # process; the kernel trace shows the GPU idle meanwhile).  A warmup of
+    # 1000 launches keeps that one-time cost out of the timed steps.
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--row-steps", type=int, default=50)
@@ -364,8 +399,10 @@ def main() -> int:
 
     P, n = 8, 134_217_728
     xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
-    dx = [up(x, dev) for x in xs]
-    dy = [torch.empty_like(t) for t in dx]
+    dx, stride = rank_slab(P, 2 * n, dev)
+    for d, x in zip(dx, xs):
+        d.copy_(torch.from_numpy(np.ascontiguousarray(x).view(np.uint8)))
+    dy, _ = rank_slab(P, 2 * n, dev)
     bytes_per_step = 2 * P * n * 2
 
     def step():
@@ -406,6 +443,8 @@ def main() -> int:
             "P": P, "count": n, "storage_dtype": "bf16", "accumulate": "f32",
             "hbm_bytes_per_step": bytes_per_step,
             "launch": "library defaults (register-direct, 4 KiB chunks, <= 3 workgroups per CU)",
+            "placement": f"each side one allocation, rank r at r x {stride} bytes "
+                         f"(256 MiB + 2 MiB + 4 KiB apart)",
             "parity_spot_check": parity,
         },
         "roofline": {

@@ -200,7 +200,7 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
                                     size_t rows, size_t hidden, const void *gamma, float eps,
                                     int dtype, void *stream, const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_AR, nranks, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RMSNORM, nranks, &l);
   if (st) return st;
   if (nranks < 1 || nranks > CCL_MAX_RANKS) return CCL_ERR_INVALID_ARG;
   if (dtype != CCL_FLOAT32 && dtype != CCL_BFLOAT16 && dtype != CCL_FLOAT16)

@@ -27,7 +27,7 @@ struct OpDefaults {
   int occupancy;
 };
 
-enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3 };
+enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3, OP_RMSNORM = 4 };
 
 inline OpDefaults default_launch(Op op, int P) {
   switch (op) {
@@ -42,6 +42,8 @@ inline OpDefaults default_launch(Op op, int P) {
       if (P >= 7 && P <= 12) return {4096, 2, 2, 3};
       if (P >= 13) return {8192, 1, 2, 1};
       return {8192, 1, 2, 3};
+    case OP_RMSNORM:
+      return {16384, 1, 1, 0};
     default:
       return {16384, 1, 4, 2};
   }

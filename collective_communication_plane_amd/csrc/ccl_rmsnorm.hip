@@ -75,11 +75,18 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// VPL = 16-byte vectors per lane per row (row_vecs <= VPL * kThreads).
-template <int DT, int PMAX, int VPL>
+// One workgroup per row (grid-strided).  The folded row is parked in dynamic
+// LDS (row_vecs 16-byte vectors, in the element type, i.e. the value a
+// reduce-scatter would hand over) between the two passes; each lane only
+// reads back the vectors it wrote, so the block-wide barriers of the norm are
+// the only synchronisation.  A lane keeps one vector per rank in flight:
+// holding several (in registers) measured slower, since more concurrent
+// streams only add DRAM page conflicts.
+template <int DT, int PMAX>
 __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int V = kVecBytes / esz;
+  extern __shared__ u32x4 row_buf[];
   __shared__ float wave_part[kThreads / 64];
   const int P = a.P;
   const bool ntl = a.flags & 1, nts = a.flags & 2;
@@ -87,24 +94,22 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
 
   for (uint64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
     const uint64_t base = row * (uint64_t)a.hidden * esz;
-    float s[VPL][8];
     float ss = 0.f;
+#pragma unroll 1
+    for (uint32_t v = threadIdx.x; v < a.row_vecs; v += kThreads) {
+      u32x4 x[PMAX];
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const uint32_t v = k * kThreads + threadIdx.x;
-      if (v < a.row_vecs) {
-        u32x4 x[PMAX];
+      for (int r = 0; r < PMAX; ++r)
+        if (r < P) {
+          const char *p = a.in[r] + base + (uint64_t)v * kVecBytes;
+          x[r] = ntl ? ld_nt(p) : ld_plain(p);
+        }
+      const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
+      row_buf[v] = sv;
+      float f[8];
+      widen_vec<DT>(sv, f);
 #pragma unroll
-        for (int r = 0; r < PMAX; ++r)
-          if (r < P) {
-            const char *p = a.in[r] + base + (uint64_t)v * kVecBytes;
-            x[r] = ntl ? ld_nt(p) : ld_plain(p);
-          }
-        // the fold, rounded to the element type as a reduce-scatter would
-        widen_vec<DT>(fold_vec<DT, CCL_SUM, PMAX>(x, P), s[k]);
-#pragma unroll
-        for (int e = 0; e < V; ++e) ss += s[k][e] * s[k][e];
-      }
+      for (int e = 0; e < V; ++e) ss += f[e] * f[e];
     }
     ss = wave_sum(ss);
     if (lane == 0) wave_part[wave] = ss;
@@ -114,44 +119,31 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
     for (int w = 0; w < kThreads / 64; ++w) total += wave_part[w];
     __syncthreads();  // wave_part is reused by the next row
     const float inv = 1.0f / sqrtf(total / (float)a.hidden + a.eps);
+#pragma unroll 2
+    for (uint32_t v = threadIdx.x; v < a.row_vecs; v += kThreads) {
+      float g[8], f[8], y[8];
+      widen_vec<DT>(ld_plain(a.gamma + (uint64_t)v * kVecBytes), g);
+      widen_vec<DT>(row_buf[v], f);
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-      const uint32_t v = k * kThreads + threadIdx.x;
-      if (v < a.row_vecs) {
-        float g[8];
-        widen_vec<DT>(ld_plain(a.gamma + (uint64_t)v * kVecBytes), g);
-        float y[8];
+      for (int e = 0; e < V; ++e) y[e] = (f[e] * inv) * g[e];
+      const u32x4 o = narrow_vec<DT>(y);
 #pragma unroll
-        for (int e = 0; e < V; ++e) y[e] = (s[k][e] * inv) * g[e];
-        const u32x4 o = narrow_vec<DT>(y);
-#pragma unroll
-        for (int q = 0; q < PMAX; ++q)
-          if (q < P) {
-            char *d = a.out[q] + base + (uint64_t)v * kVecBytes;
-            if (nts) st_nt(d, o);
-            else st_plain(d, o);
-          }
-      }
+      for (int q = 0; q < PMAX; ++q)
+        if (q < P) {
+          char *d = a.out[q] + base + (uint64_t)v * kVecBytes;
+          if (nts) st_nt(d, o);
+          else st_plain(d, o);
+        }
     }
   }
 }
 
-template <int DT, int PMAX>
-hipError_t launch_vpl(const RmsArgs &a, int vpl, unsigned grid, size_t lds, hipStream_t st) {
-  switch (vpl) {
-    case 1: hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, PMAX, 1>), dim3(grid), dim3(kThreads), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, PMAX, 2>), dim3(grid), dim3(kThreads), lds, st, a); break;
-    case 4: hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, PMAX, 4>), dim3(grid), dim3(kThreads), lds, st, a); break;
-    default: hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, PMAX, 8>), dim3(grid), dim3(kThreads), lds, st, a); break;
-  }
-  return hipGetLastError();
-}
-
 template <int DT>
-hipError_t launch_p(const RmsArgs &a, int vpl, unsigned grid, size_t lds, hipStream_t st) {
-  if (a.P <= 4) return launch_vpl<DT, 4>(a, vpl, grid, lds, st);
-  if (a.P <= 8) return launch_vpl<DT, 8>(a, vpl, grid, lds, st);
-  return launch_vpl<DT, 16>(a, vpl, grid, lds, st);
+hipError_t launch_p(const RmsArgs &a, unsigned grid, size_t lds, hipStream_t st) {
+  if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16>), dim3(grid), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -170,16 +162,16 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   a.eps = d.eps;
   a.P = d.P;
   a.flags = (l.nt_load ? 1 : 0) | (l.nt_store ? 2 : 0);
-  const uint32_t need = (a.row_vecs + kThreads - 1) / kThreads;
-  const int vpl = need <= 1 ? 1 : need <= 2 ? 2 : need <= 4 ? 4 : 8;
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : d.rows;
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, d.rows), 1u << 30);
-  const size_t lds = occupancy_lds(l.occupancy, (kThreads / 64) * sizeof(float));
+  // the row buffer, or more when the launch caps residency through LDS
+  const size_t row_lds = (size_t)a.row_vecs * kVecBytes;
+  const size_t lds = std::max(row_lds, occupancy_lds(l.occupancy, (kThreads / 64) * sizeof(float)));
   hipError_t err;
   switch (d.dtype) {
-    case CCL_FLOAT32: err = launch_p<CCL_FLOAT32>(a, vpl, (unsigned)grid, lds, stream); break;
-    case CCL_BFLOAT16: err = launch_p<CCL_BFLOAT16>(a, vpl, (unsigned)grid, lds, stream); break;
-    default: err = launch_p<CCL_FLOAT16>(a, vpl, (unsigned)grid, lds, stream); break;
+    case CCL_FLOAT32: err = launch_p<CCL_FLOAT32>(a, (unsigned)grid, lds, stream); break;
+    case CCL_BFLOAT16: err = launch_p<CCL_BFLOAT16>(a, (unsigned)grid, lds, stream); break;
+    default: err = launch_p<CCL_FLOAT16>(a, (unsigned)grid, lds, stream); break;
   }
   return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

@@ -77,6 +77,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
  *   reshard copy    16 KiB chunks, <= 2 WGs per CU
+ *   all-reduce + RMSNorm  one workgroup per row, residency bounded only by
+ *                   registers and the row buffer it keeps in LDS; it reads
+ *                   workgroups, nontemporal and occupancy and ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
  * use a register-direct kernel that realigns the inputs in VGPRs.
  * A zero field means "the default for this call"; out-of-range values give
