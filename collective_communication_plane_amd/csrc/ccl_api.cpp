@@ -92,7 +92,8 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
     if (cfg->occupancy < 0 || cfg->occupancy > 32 || cfg->reserved != 0) return CCL_ERR_INVALID_ARG;
     if (cfg->occupancy) l.occupancy = cfg->occupancy;
   }
-  if (op == OP_RESHARD && explicit_stages && l.stages != 1) return CCL_ERR_UNSUPPORTED;
+  if ((op == OP_RESHARD || op == OP_RESHARD_FP8) && explicit_stages && l.stages != 1)
+    return CCL_ERR_UNSUPPORTED;
   if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) {
     if (explicit_stages) return CCL_ERR_INVALID_ARG;
     l.stages = 1;
@@ -319,7 +320,7 @@ ccl_status_t ccl_reshard_copy_fp8(const ccl_plan_t *plan, const void *const *src
                                   void *const *dst_codes, float *const *dst_scales, void *stream,
                                   const ccl_launch_config_t *cfg) {
   ccl::Launch l;
-  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD, 0, &l);
+  ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RESHARD_FP8, 0, &l);
   if (st) return st;
   if (!plan || !src_bufs || !dst_codes || !dst_scales) return CCL_ERR_INVALID_ARG;
   ccl_plan *p = const_cast<ccl_plan *>(plan);

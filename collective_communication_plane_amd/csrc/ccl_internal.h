@@ -27,7 +27,7 @@ struct OpDefaults {
   int occupancy;
 };
 
-enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3, OP_RMSNORM = 4 };
+enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3, OP_RMSNORM = 4, OP_RESHARD_FP8 = 5 };
 
 inline OpDefaults default_launch(Op op, int P) {
   switch (op) {
@@ -44,6 +44,8 @@ inline OpDefaults default_launch(Op op, int P) {
       return {8192, 1, 2, 3};
     case OP_RMSNORM:
       return {16384, 1, 1, 0};
+    case OP_RESHARD_FP8:
+      return {65536, 1, 2, 0};
     default:
       return {16384, 1, 4, 2};
   }

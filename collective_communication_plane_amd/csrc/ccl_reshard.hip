@@ -133,6 +133,7 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
 // shuffles, and store codes and scale to every replica.
 
 constexpr int kFp8Block = 128;
+constexpr int kRhoRegs = 4;  // replicas whose destinations a chunk keeps in registers
 
 struct ReshardFp8Args {
   const char *src[CCL_MAX_MESH_RANKS];
@@ -148,21 +149,57 @@ struct ReshardFp8Args {
   int flags;
 };
 
-// fp32 -> E4M3 code, round to nearest even, saturating; |y| must not be NaN.
-__device__ __forceinline__ uint32_t e4m3_rne_sat(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fabsf(y);
-  if (!(a < 448.0f)) return sign | 0x7eu;
-  if (a < 0.015625f) {  // below 2^-6: a multiple of 2^-9, exact scaling then RNE
-    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  const uint32_t ua = __float_as_uint(a);
-  const uint32_t r = ua + 0x7ffffu + ((ua >> 20) & 1u);  // keep 3 mantissa bits
-  const uint32_t e = (r >> 23) - 127u + 7u;
-  return sign | (e << 3) | ((r >> 20) & 7u);
+// x / scale correctly rounded, from rcp = RN(1 / scale) and two fma residual
+// corrections: the first brings the product within one ulp of the quotient,
+// the second then rounds correctly (Markstein's theorem for round-to-nearest:
+// a quotient within one ulp, corrected once by its exact residual times the
+// correctly rounded reciprocal).  It needs the residuals to stay normal, which
+// holds for every quotient that can reach a nonzero code when
+// 2^-60 <= scale <= 2^64; the kernel divides outside that range.  A zero
+// quotient's sign is taken from x.
+__device__ __forceinline__ float quot_rcp(float x, float scale, float rcp) {
+  float q = x * rcp;
+  float r = fmaf(-scale, q, x);
+  q = fmaf(r, rcp, q);
+  r = fmaf(-scale, q, x);
+  return copysignf(fmaf(r, rcp, q), x);
 }
 
-template <int DT>
+// Maximum over each aligned group of N (16 or 32) lanes, left in every lane
+// of the group; all 64 lanes must be active.  Within a 16-lane DPP row:
+// swap neighbours, swap pairs (each lane now holds its quad's maximum), then
+// the row's half-mirror and full mirror pair every lane with a lane of the
+// other quad / other half.  A 32-lane group adds an exchange between its two
+// rows (swizzle with lane xor 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return fmaxf(v, __int_as_float(o));
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141>(v);  // row_half_mirror
+  v = dpp_max<0x140>(v);  // row_mirror
+  if constexpr (N == 32)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  return v;
+}
+
+// Two quotients -> two E4M3 codes (OCP: bias 7, largest finite 448), round to
+// nearest even with subnormal codes, magnitudes above 448 saturated, packed
+// into the low (HI false) or high half of `word`.  gfx950's conversion
+// implements exactly this rounding on values already clamped to +-448.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t word) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
+}
+
+// U = 16-byte vectors each lane loads before it processes any of them.
+template <int DT, int U>
 __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int EPL = kVecBytes / esz;             // elements per lane
@@ -177,58 +214,96 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
     const int32_t *rep = a.rep + (uint64_t)iv.dst_shard * a.rho;
     const uint64_t elem0 = (iv.dst_off + off) / esz;  // first destination element, block-aligned
     const uint64_t nvec = (bytes + kVecBytes - 1) / kVecBytes;
-    // whole groups iterate together so shuffles see every lane of a block
-    for (uint64_t v0 = 0; v0 < nvec; v0 += kThreads) {
-      const uint64_t v = v0 + threadIdx.x;
-      const bool live = v * kVecBytes < bytes;
-      float x[EPL];
-      float amax = 0.f;
-      if (live) {
-        const u32x4 w = ntl ? ld_nt(src + v * kVecBytes) : ld_plain(src + v * kVecBytes);
+    // The first kRhoRegs replicas' destinations, resolved once per chunk
+    // rather than through the argument tables at every store.
+    char *cdst[kRhoRegs];
+    float *sdst[kRhoRegs];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if constexpr (DT == CCL_FLOAT32) {
-            x[k] = __uint_as_float(w[k]);
-          } else if constexpr (DT == CCL_BFLOAT16) {
-            x[2 * k] = bf16_lo(w[k]);
-            x[2 * k + 1] = bf16_hi(w[k]);
-          } else {
-            x[2 * k] = f16_lo(w[k]);
-            x[2 * k + 1] = f16_hi(w[k]);
-          }
-        }
-        // a short last block: elements past the interval do not count
-        const uint64_t valid = min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz);
+    for (int j = 0; j < kRhoRegs; ++j)
+      if (j < a.rho) {
+        cdst[j] = a.codes[rep[j]] + elem0;
+        sdst[j] = a.scales[rep[j]] + elem0 / kFp8Block;
+      }
+    // Whole groups iterate together so shuffles see every lane of a block;
+    // vector v0 + u * kThreads + lane keeps each block on LPB adjacent lanes.
+    for (uint64_t v0 = 0; v0 < nvec; v0 += (uint64_t)kThreads * U) {
+      u32x4 w[U];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          if ((uint64_t)e < valid) amax = fmaxf(amax, fabsf(x[e]));
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = v0 + (uint64_t)u * kThreads + threadIdx.x;
+        if (v < nvec) w[u] = ntl ? ld_nt(src + v * kVecBytes) : ld_plain(src + v * kVecBytes);
       }
 #pragma unroll
-      for (int m = LPB / 2; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
-      if (!live) continue;
-      const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
-      const uint64_t valid = min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz);
-      uint32_t q[EPL];
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = v0 + (uint64_t)u * kThreads + threadIdx.x;
+        const bool live = v < nvec;
+        float x[EPL];
+        float amax = 0.f;
+        // a short last block: elements past the interval do not count
+        const uint32_t valid = live ? (uint32_t)min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz) : 0u;
+        if (live) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) q[e] = e4m3_rne_sat(x[e] / scale);
-      const uint64_t elem = elem0 + v * EPL;
-      for (int j = 0; j < a.rho; ++j) {
-        char *d = a.codes[rep[j]] + elem;
-        if (valid == (uint64_t)EPL) {
-          if constexpr (EPL == 8) {
-            uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-            uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-            *(uint2 *)d = make_uint2(lo, hi);
-          } else {
-            *(uint32_t *)d = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+          for (int k = 0; k < 4; ++k) {
+            if constexpr (DT == CCL_FLOAT32) {
+              x[k] = __uint_as_float(w[u][k]);
+            } else if constexpr (DT == CCL_BFLOAT16) {
+              x[2 * k] = bf16_lo(w[u][k]);
+              x[2 * k + 1] = bf16_hi(w[u][k]);
+            } else {
+              x[2 * k] = f16_lo(w[u][k]);
+              x[2 * k + 1] = f16_hi(w[u][k]);
+            }
           }
-        } else {
-          for (uint64_t e = 0; e < valid; ++e) d[e] = (char)q[e];
+          if (valid == (uint32_t)EPL) {  // every vector but a chunk's last
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              if ((uint32_t)e < valid) amax = fmaxf(amax, fabsf(x[e]));
+          }
         }
-        if ((threadIdx.x % LPB) == 0) a.scales[rep[j]][elem / kFp8Block] = scale;
+        amax = group_max<LPB>(amax);
+        if (!live) continue;  // every lane has taken part in this vector's shuffles
+        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        float y[EPL];
+        if (scale >= 0x1p-60f && scale <= 0x1p64f) {
+          const float rcp = 1.0f / scale;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) y[e] = quot_rcp(x[e], scale, rcp);
+        } else {
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) y[e] = x[e] / scale;
+        }
+        const uint64_t e_off = v * EPL;  // element offset in the chunk's destination run
+        const uint32_t lo = e4m3_pack2<true>(y[2], y[3], e4m3_pack2<false>(y[0], y[1], 0u));
+        uint32_t hi = 0;
+        if constexpr (EPL == 8) hi = e4m3_pack2<true>(y[6], y[7], e4m3_pack2<false>(y[4], y[5], 0u));
+        const bool lead = (threadIdx.x % LPB) == 0;
+        auto put = [&](char *d, float *sc) {
+          if (valid == (uint32_t)EPL) {
+            if constexpr (EPL == 8) *(uint2 *)(d + e_off) = make_uint2(lo, hi);
+            else *(uint32_t *)(d + e_off) = lo;
+          } else {
+            for (uint32_t e = 0; e < valid; ++e) d[e_off + e] = (char)((e < 4 ? lo : hi) >> (8 * (e & 3)));
+          }
+          if (lead) sc[e_off / kFp8Block] = scale;
+        };
+#pragma unroll
+        for (int j = 0; j < kRhoRegs; ++j)
+          if (j < a.rho) put(cdst[j], sdst[j]);
+        for (int j = kRhoRegs; j < a.rho; ++j)
+          put(a.codes[rep[j]] + elem0, a.scales[rep[j]] + elem0 / kFp8Block);
       }
     }
   }
+}
+
+template <int DT>
+void launch_fp8_u(const ReshardFp8Args &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
+  if (unroll >= 4) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (unroll == 2) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 2>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((reshard_fp8_kernel<DT, 1>), dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 // Build (or find) the device copy of the plan for this device and chunk size.
@@ -348,15 +423,9 @@ ccl_status_t reshard_fp8_launch(ccl_plan *p, const void *const *src, void *const
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
   const size_t lds = occupancy_lds(l.occupancy, 0);
   switch (p->dtype) {
-    case CCL_FLOAT32:
-      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_FLOAT32>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
-      break;
-    case CCL_BFLOAT16:
-      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_BFLOAT16>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL(reshard_fp8_kernel<CCL_FLOAT16>, dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
-      break;
+    case CCL_FLOAT32: launch_fp8_u<CCL_FLOAT32>(a, l.unroll, (unsigned)grid, lds, stream); break;
+    case CCL_BFLOAT16: launch_fp8_u<CCL_BFLOAT16>(a, l.unroll, (unsigned)grid, lds, stream); break;
+    default: launch_fp8_u<CCL_FLOAT16>(a, l.unroll, (unsigned)grid, lds, stream); break;
   }
   return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

@@ -76,7 +76,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
- *   reshard copy    16 KiB chunks, <= 2 WGs per CU
+ *   reshard copy    16 KiB chunks, unroll 4, <= 2 WGs per CU
+ *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
+ *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  one workgroup per row, residency bounded only by
  *                   registers and the row buffer it keeps in LDS; it reads
  *                   workgroups, nontemporal and occupancy and ignores the rest
@@ -99,7 +101,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                consumer waves fold and store them (clamped so the ring
  *                fits in 128 KiB).  The reshard copy is register-direct only.
  *   unroll       register-direct only: 16-byte vectors each lane keeps in
- *                flight per rank (1, 2 or 4; 4 is used as 2 when P > 8).
+ *                flight per rank (1, 2 or 4; 4 is used as 2 when P > 8); for
+ *                the fp8 reshard, vectors each lane loads before quantizing.
  *   nontemporal  bit 0: nontemporal loads, bit 1: nontemporal stores;
  *                0 = default (both), 4 = neither.
  *   occupancy    at most this many workgroups resident per compute unit
@@ -313,7 +316,9 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
  * bias 7, largest finite 448) plus one fp32 scale per block of 128
  * consecutive elements of its local buffer: scale = amax / 448 in fp32 (1 for
  * an all-zero block), code = round-to-nearest-even of x / scale in fp32,
- * saturated to +-448.  Dequantize as code_value * scale.
+ * saturated to +-448.  Dequantize as code_value * scale.  Source elements
+ * must be finite: a block holding a NaN or an infinity gets unspecified
+ * codes and scale.
  *
  *   src_bufs    as for ccl_reshard_copy (element type: fp32, bf16 or fp16).
  *   dst_codes   one pointer per destination-mesh rank, local-element-count

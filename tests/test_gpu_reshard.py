@@ -239,6 +239,123 @@ def test_reshard_fp8_matches_oracle(case, dtype):
         ccl.check(ccl.ccl_plan_destroy(plan))
 
 
+def _to_dtype(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """fp32 values -> the element type's storage (round to nearest even)."""
+    if dtype == "f32":
+        return x32.astype(np.float32)
+    if dtype == "f16":
+        with np.errstate(over="ignore"):
+            return x32.astype(np.float16).view(np.uint16)
+    return si.to_bf16_bits(x32)
+
+
+def _as_f32(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return si.bf16_bits_to_f32(a)
+    return a.view(np.float16).astype(np.float32) if dtype == "f16" else a.astype(np.float32)
+
+
+def _neighbours(a: np.ndarray, dtype: str, step: int) -> np.ndarray:
+    """The storage values `step` ulps away (same sign, away from zero if step > 0)."""
+    if dtype == "f32":
+        return (a.view(np.uint32) + np.uint32(step) if step > 0 else
+                a.view(np.uint32) - np.uint32(-step)).view(np.float32)
+    return (a.view(np.uint16).astype(np.int32) + step).astype(np.uint16)
+
+
+def _pad128(b: np.ndarray) -> np.ndarray:
+    """Fill a block up to 128 elements by repeating its own values."""
+    while b.size < 128:
+        b = np.concatenate([b, b[: 128 - b.size]])
+    return b
+
+
+def _fp8_edge_blocks(dtype: str, rng) -> list:
+    """128-element blocks aimed at the quantizer's decisions: E4M3 midpoints
+    after an exact (power-of-two) scale, one ulp either side of them, quotients
+    next to midpoints under an inexact scale, signed zeros, subnormal inputs,
+    and block maxima that put the scale at or past [2^-60, 2^64]."""
+    vals = [oracle.e4m3_value(c) for c in range(0x7F)]
+    mids = np.array([(vals[i] + vals[i + 1]) / 2 for i in range(0x7E)], np.float64)
+    f16 = dtype == "f16"
+    blocks = []
+
+    def block(head, body):
+        body = np.asarray(body, np.float32)
+        b = np.concatenate([np.asarray(head, np.float32), body])[:128]
+        if b.size < 128:
+            b = np.concatenate([b, rng.permutation(body)[: 128 - b.size] if body.size else
+                                np.zeros(128 - b.size, np.float32)])
+        while b.size < 128:
+            b = np.concatenate([b, b[: 128 - b.size]])
+        return _to_dtype(b.astype(np.float32), dtype)
+
+    exps = [0, -3, 5] + ([] if f16 else [-40, 40])
+    for k in exps:
+        s = 2.0 ** k
+        sign = np.where(np.arange(mids.size) % 2 == 0, 1.0, -1.0)
+        tie = block([448 * s, -448 * s], mids * s * sign)          # exact ties
+        blocks.append(tie)
+        for step in (1, -1):                                       # one ulp off a tie
+            body = _neighbours(_to_dtype((mids * s).astype(np.float32), dtype), dtype, step)
+            blocks.append(_pad128(np.concatenate([_to_dtype(np.array([448 * s], np.float32),
+                                                            dtype), body])))
+    for amax in (3.7, 0.0173, 250.0) if f16 else (3.7, 0.0173, 1.0e5, 7.3e-20):
+        a = float(_as_f32(_to_dtype(np.array([amax], np.float32), dtype), dtype)[0])
+        scale = np.float32(np.float32(a) / np.float32(448.0))
+        near = _to_dtype((mids * np.float64(scale)).astype(np.float32), dtype)
+        blocks.append(_pad128(np.concatenate([_to_dtype(np.array([a], np.float32), dtype), near])))
+    zeros = np.where(np.arange(128) % 3 == 0, -0.0, 0.0).astype(np.float32)
+    blocks.append(_to_dtype(zeros, dtype))                                  # all-zero block
+    mixed = rng.standard_normal(128).astype(np.float32)
+    mixed[::5] = -0.0
+    mixed[1::7] = 0.0
+    blocks.append(_to_dtype(mixed, dtype))                                  # signed zeros
+    tiny = 2.0 ** -20 if f16 else 2.0 ** -130                               # subnormal inputs
+    blocks.append(block([4 * tiny], rng.integers(-4, 5, 200) * tiny))
+    if not f16:
+        for amax in (2.0 ** -70, 448 * 2.0 ** -60, 2.0 ** 80, 448 * 2.0 ** 64):
+            a = np.float32(amax)
+            lo = np.nextafter(a, np.float32(0)) if dtype == "f32" else a
+            body = (rng.uniform(-1, 1, 300) * a).astype(np.float32)
+            blocks.append(block([a], body))
+            if dtype == "f32":
+                blocks.append(block([lo], (body * np.float32(0.5)).astype(np.float32)))
+    return blocks
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_reshard_fp8_edge_values(dtype):
+    rng = np.random.default_rng(77)
+    blocks = _fp8_edge_blocks(dtype, rng)
+    nb = (len(blocks) + 1) // 2 * 2
+    while len(blocks) < nb:
+        blocks.append(blocks[0])
+    G = np.concatenate(blocks).reshape(2, -1)       # two rows of whole blocks
+    shape = G.shape
+    src = ([1], 0, ["R"])
+    dst = ([2, 2], 1, ["R", ("S", 0)])              # two shards (a row each), two replicas
+    want = oracle.reshard_fp8(shape, src, dst, [G.ravel()], dtype)
+    plan = make_plan(shape, ccl.DTYPES[dtype], src, dst)
+    try:
+        dsrc = upload_all([G.ravel()], DEV)
+        codes = [DevBuf(w[0].size, DEV) for w in want]
+        scales = [DevBuf(w[1].nbytes, DEV) for w in want]
+        ccl.check(ccl.ccl_reshard_copy_fp8(plan, [b.ptr for b in dsrc], [b.ptr for b in codes],
+                                           [b.ptr for b in scales], torch.cuda.current_stream()),
+                  "reshard_copy_fp8")
+        torch.cuda.synchronize()
+        for c, f, (wc, wf) in zip(codes, scales, want):
+            assert c.guards_intact() and f.guards_intact()
+            np.testing.assert_array_equal(f.download(np.float32).view(np.uint32), wf.view(np.uint32))
+            got = c.download(np.uint8)
+            bad = np.nonzero(got != wc)[0]
+            assert bad.size == 0, (f"{bad.size} codes differ, first at {bad[0]}: "
+                                   f"got {got[bad[0]]:#x} want {wc[bad[0]]:#x}")
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+
+
 def test_reshard_fp8_rejects_split_blocks():
     # rows of 100 elements: the MoE-like column split cuts 128-element blocks
     plan = make_plan((16, 100), ccl.CCL_BFLOAT16, ([2], 0, [("S", 0)]), ([2], 2, [("S", 1)]))
