@@ -20,6 +20,20 @@ __device__ __forceinline__ u32x4 ld_nt(const char *p) {
 __device__ __forceinline__ void st_plain(char *p, u32x4 v) { *(u32x4 *)p = v; }
 __device__ __forceinline__ void st_nt(char *p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4 *)p); }
 
+// The hint as a compile-time choice.  Selecting between ld_nt and ld_plain
+// (or st_nt and st_plain) with a runtime flag is not enough: the compiler
+// merges the two accesses into one and drops the nontemporal hint.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const char *p) {
+  if constexpr (NT) return ld_nt(p);
+  else return ld_plain(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st(char *p, u32x4 v) {
+  if constexpr (NT) st_nt(p, v);
+  else st_plain(p, v);
+}
+
 // bf16 -> fp32 is exact: the bf16 pattern is the upper half of the fp32 one.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -48,7 +48,6 @@ struct ReshardArgs {
   uint64_t chunk_bytes;
   int n_iv;
   int rho;
-  int flags;           // bit 0: nontemporal loads, bit 1: nontemporal stores
   int aligned;         // every base and interval offset is 16-byte aligned
 };
 
@@ -62,8 +61,9 @@ __device__ __forceinline__ int find_interval(const DevInterval *iv, int n, uint6
   return lo;
 }
 
+// NTL / NTS: nontemporal loads / stores (template arguments, see ld / st).
+template <bool NTL, bool NTS>
 __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int i = a.chunk_iv ? (int)a.chunk_iv[c] : find_interval(a.iv, a.n_iv, c);
     const DevInterval iv = a.iv[i];
@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
 #pragma unroll
       for (int u = 0; u < kReshardUnroll; ++u) {
         const uint64_t vv = v + (uint64_t)u * kThreads;
-        if (vv < nvec) x[u] = ntl ? ld_nt(vs + vv * kVecBytes) : ld_plain(vs + vv * kVecBytes);
+        if (vv < nvec) x[u] = ld<NTL>(vs + vv * kVecBytes);
       }
       for (int j = 0; j < a.rho; ++j) {
         char *d = a.dst[rep[j]] + dst_base + head;
@@ -111,8 +111,7 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
         for (int u = 0; u < kReshardUnroll; ++u) {
           const uint64_t vv = v + (uint64_t)u * kThreads;
           if (vv < nvec) {
-            if (nts) st_nt(d + vv * kVecBytes, x[u]);
-            else st_plain(d + vv * kVecBytes, x[u]);
+            st<NTS>(d + vv * kVecBytes, x[u]);
           }
         }
       }
@@ -146,7 +145,6 @@ struct ReshardFp8Args {
   uint64_t chunk_bytes;  // source bytes per chunk, a multiple of the block's bytes
   int n_iv;
   int rho;
-  int flags;
 };
 
 // x / scale correctly rounded, from rcp = RN(1 / scale) and two fma residual
@@ -198,13 +196,13 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t word) 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
 }
 
-// U = 16-byte vectors each lane loads before it processes any of them.
-template <int DT, int U>
+// U = 16-byte vectors each lane loads before it processes any of them;
+// NTL / NTS: nontemporal source loads / code stores.
+template <int DT, int U, bool NTL, bool NTS>
 __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int EPL = kVecBytes / esz;             // elements per lane
   constexpr int LPB = kFp8Block / EPL;             // lanes per block (16 or 32)
-  const bool ntl = a.flags & 1;
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int i = a.chunk_iv ? (int)a.chunk_iv[c] : find_interval(a.iv, a.n_iv, c);
     const DevInterval iv = a.iv[i];
@@ -231,7 +229,7 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kThreads + threadIdx.x;
-        if (v < nvec) w[u] = ntl ? ld_nt(src + v * kVecBytes) : ld_plain(src + v * kVecBytes);
+        if (v < nvec) w[u] = ld<NTL>(src + v * kVecBytes);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -282,8 +280,17 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
         const bool lead = (threadIdx.x % LPB) == 0;
         auto put = [&](char *d, float *sc) {
           if (valid == (uint32_t)EPL) {
-            if constexpr (EPL == 8) *(uint2 *)(d + e_off) = make_uint2(lo, hi);
-            else *(uint32_t *)(d + e_off) = lo;
+            if constexpr (EPL == 8) {
+              typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+              u32x2 w2;
+              w2[0] = lo;
+              w2[1] = hi;
+              if constexpr (NTS) __builtin_nontemporal_store(w2, (u32x2 *)(d + e_off));
+              else *(u32x2 *)(d + e_off) = w2;
+            } else {
+              if constexpr (NTS) __builtin_nontemporal_store(lo, (uint32_t *)(d + e_off));
+              else *(uint32_t *)(d + e_off) = lo;
+            }
           } else {
             for (uint32_t e = 0; e < valid; ++e) d[e_off + e] = (char)((e < 4 ? lo : hi) >> (8 * (e & 3)));
           }
@@ -299,11 +306,19 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
   }
 }
 
-template <int DT>
+template <int DT, bool NTL, bool NTS>
 void launch_fp8_u(const ReshardFp8Args &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
-  if (unroll >= 4) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 4>), dim3(grid), dim3(kThreads), lds, st, a);
-  else if (unroll == 2) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 2>), dim3(grid), dim3(kThreads), lds, st, a);
-  else hipLaunchKernelGGL((reshard_fp8_kernel<DT, 1>), dim3(grid), dim3(kThreads), lds, st, a);
+  if (unroll >= 4) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (unroll == 2) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 2, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((reshard_fp8_kernel<DT, 1, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+}
+
+template <int DT>
+void launch_fp8_dt(const ReshardFp8Args &a, const Launch &l, unsigned grid, size_t lds, hipStream_t st) {
+  if (l.nt_load && l.nt_store) launch_fp8_u<DT, true, true>(a, l.unroll, grid, lds, st);
+  else if (l.nt_load) launch_fp8_u<DT, true, false>(a, l.unroll, grid, lds, st);
+  else if (l.nt_store) launch_fp8_u<DT, false, true>(a, l.unroll, grid, lds, st);
+  else launch_fp8_u<DT, false, false>(a, l.unroll, grid, lds, st);
 }
 
 // Build (or find) the device copy of the plan for this device and chunk size.
@@ -386,11 +401,14 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   a.chunk_bytes = l.chunk_bytes;
   a.n_iv = (int)p->intervals.size();
   a.rho = p->n_dst / p->n_dst_shards;
-  a.flags = (l.nt_load ? 1 : 0) | (l.nt_store ? 2 : 0);
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
-  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kThreads),
-                     occupancy_lds(l.occupancy, 0), stream, a);
+  const size_t lds = occupancy_lds(l.occupancy, 0);
+  const dim3 g((unsigned)grid), b(kThreads);
+  if (l.nt_load && l.nt_store) hipLaunchKernelGGL((reshard_kernel<true, true>), g, b, lds, stream, a);
+  else if (l.nt_load) hipLaunchKernelGGL((reshard_kernel<true, false>), g, b, lds, stream, a);
+  else if (l.nt_store) hipLaunchKernelGGL((reshard_kernel<false, true>), g, b, lds, stream, a);
+  else hipLaunchKernelGGL((reshard_kernel<false, false>), g, b, lds, stream, a);
   return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
 
@@ -418,14 +436,13 @@ ccl_status_t reshard_fp8_launch(ccl_plan *p, const void *const *src, void *const
   a.chunk_bytes = chunk;
   a.n_iv = (int)p->intervals.size();
   a.rho = p->n_dst / p->n_dst_shards;
-  a.flags = l.nt_load ? 1 : 0;
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : a.total_chunks;
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
   const size_t lds = occupancy_lds(l.occupancy, 0);
   switch (p->dtype) {
-    case CCL_FLOAT32: launch_fp8_u<CCL_FLOAT32>(a, l.unroll, (unsigned)grid, lds, stream); break;
-    case CCL_BFLOAT16: launch_fp8_u<CCL_BFLOAT16>(a, l.unroll, (unsigned)grid, lds, stream); break;
-    default: launch_fp8_u<CCL_FLOAT16>(a, l.unroll, (unsigned)grid, lds, stream); break;
+    case CCL_FLOAT32: launch_fp8_dt<CCL_FLOAT32>(a, l, (unsigned)grid, lds, stream); break;
+    case CCL_BFLOAT16: launch_fp8_dt<CCL_BFLOAT16>(a, l, (unsigned)grid, lds, stream); break;
+    default: launch_fp8_dt<CCL_FLOAT16>(a, l, (unsigned)grid, lds, stream); break;
   }
   return hipGetLastError() == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

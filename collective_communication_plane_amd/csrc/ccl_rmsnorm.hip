@@ -29,7 +29,6 @@ struct RmsArgs {
   uint32_t row_vecs;   // 16-byte vectors per row
   float eps;
   int P;
-  int flags;           // bit 0: nontemporal loads, bit 1: nontemporal stores
 };
 
 // Up to 8 elements per 16-byte vector; fp32 uses the first 4.
@@ -82,14 +81,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the only synchronisation.  A lane keeps one vector per rank in flight:
 // holding several (in registers) measured slower, since more concurrent
 // streams only add DRAM page conflicts.
-template <int DT, int PMAX>
+// NTL / NTS: nontemporal loads / stores (template arguments, see ld / st).
+template <int DT, int PMAX, bool NTL, bool NTS>
 __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int V = kVecBytes / esz;
   extern __shared__ u32x4 row_buf[];
   __shared__ float wave_part[kThreads / 64];
   const int P = a.P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   for (uint64_t row = blockIdx.x; row < a.rows; row += gridDim.x) {
@@ -102,7 +101,7 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
       for (int r = 0; r < PMAX; ++r)
         if (r < P) {
           const char *p = a.in[r] + base + (uint64_t)v * kVecBytes;
-          x[r] = ntl ? ld_nt(p) : ld_plain(p);
+          x[r] = ld<NTL>(p);
         }
       const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
       row_buf[v] = sv;
@@ -131,19 +130,26 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
       for (int q = 0; q < PMAX; ++q)
         if (q < P) {
           char *d = a.out[q] + base + (uint64_t)v * kVecBytes;
-          if (nts) st_nt(d, o);
-          else st_plain(d, o);
+          st<NTS>(d, o);
         }
     }
   }
 }
 
-template <int DT>
+template <int DT, bool NTL, bool NTS>
 hipError_t launch_p(const RmsArgs &a, unsigned grid, size_t lds, hipStream_t st) {
-  if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4>), dim3(grid), dim3(kThreads), lds, st, a);
-  else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8>), dim3(grid), dim3(kThreads), lds, st, a);
-  else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16>), dim3(grid), dim3(kThreads), lds, st, a);
+  if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_nt(const RmsArgs &a, const Launch &l, unsigned grid, size_t lds, hipStream_t st) {
+  if (l.nt_load && l.nt_store) return launch_p<DT, true, true>(a, grid, lds, st);
+  if (l.nt_load) return launch_p<DT, true, false>(a, grid, lds, st);
+  if (l.nt_store) return launch_p<DT, false, true>(a, grid, lds, st);
+  return launch_p<DT, false, false>(a, grid, lds, st);
 }
 
 }  // namespace
@@ -161,7 +167,6 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   a.row_vecs = (uint32_t)(d.hidden * esz / kVecBytes);
   a.eps = d.eps;
   a.P = d.P;
-  a.flags = (l.nt_load ? 1 : 0) | (l.nt_store ? 2 : 0);
   uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : d.rows;
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, d.rows), 1u << 30);
   // the row buffer, or more when the launch caps residency through LDS
@@ -169,9 +174,9 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   const size_t lds = std::max(row_lds, occupancy_lds(l.occupancy, (kThreads / 64) * sizeof(float)));
   hipError_t err;
   switch (d.dtype) {
-    case CCL_FLOAT32: err = launch_p<CCL_FLOAT32>(a, (unsigned)grid, lds, stream); break;
-    case CCL_BFLOAT16: err = launch_p<CCL_BFLOAT16>(a, (unsigned)grid, lds, stream); break;
-    default: err = launch_p<CCL_FLOAT16>(a, (unsigned)grid, lds, stream); break;
+    case CCL_FLOAT32: err = launch_nt<CCL_FLOAT32>(a, l, (unsigned)grid, lds, stream); break;
+    case CCL_BFLOAT16: err = launch_nt<CCL_BFLOAT16>(a, l, (unsigned)grid, lds, stream); break;
+    default: err = launch_nt<CCL_FLOAT16>(a, l, (unsigned)grid, lds, stream); break;
   }
   return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

@@ -76,8 +76,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
- *   reshard copy    16 KiB chunks, unroll 4, <= 2 WGs per CU
- *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
+ *   reshard copy    32 KiB chunks, unroll 4, <= 2 WGs per CU
+ *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  one workgroup per row, residency bounded only by
  *                   registers and the row buffer it keeps in LDS; it reads
