@@ -106,6 +106,29 @@ def test_reshard_launch_config_does_not_change_results(chunk, wgs):
         ccl.check(ccl.ccl_plan_destroy(plan))
 
 
+# every nontemporal choice is its own kernel instantiation
+@pytest.mark.parametrize("cfg", [dict(nontemporal=1), dict(nontemporal=2), dict(nontemporal=4),
+                                 dict(nontemporal=4, unroll=1, occupancy=32),
+                                 dict(nontemporal=2, unroll=2, chunk_bytes=8192)])
+def test_reshard_nontemporal_variants(cfg):
+    shape, src, dst = CASES[8]
+    G = si.tensor(shape, "bf16", "w002", seed=98)
+    src_bufs = local_blocks(G, src)
+    want = oracle.reshard(shape, src, dst, src_bufs)
+    plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
+    try:
+        dsrc = upload_all(src_bufs, DEV)
+        ddst = [DevBuf(w.nbytes, DEV) for w in want]
+        ccl.check(ccl.ccl_reshard_copy(plan, [b.ptr for b in dsrc], [b.ptr for b in ddst],
+                                       torch.cuda.current_stream(), ccl.LaunchConfig(**cfg)))
+        torch.cuda.synchronize()
+        for b, w in zip(ddst, want):
+            assert b.guards_intact()
+            np.testing.assert_array_equal(b.download(w.dtype), w)
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+
+
 def test_reshard_rejects_overlapping_buffers():
     shape, src, dst = CASES[0]
     plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
@@ -352,6 +375,32 @@ def test_reshard_fp8_edge_values(dtype):
             bad = np.nonzero(got != wc)[0]
             assert bad.size == 0, (f"{bad.size} codes differ, first at {bad[0]}: "
                                    f"got {got[bad[0]]:#x} want {wc[bad[0]]:#x}")
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("cfg", [dict(unroll=1), dict(unroll=4), dict(nontemporal=1),
+                                 dict(nontemporal=2), dict(nontemporal=4, unroll=1),
+                                 dict(chunk_bytes=1024, workgroups=3), dict(occupancy=2)])
+def test_reshard_fp8_launch_variants(cfg, dtype):
+    shape, src, dst = FP8_CASES[1]
+    G = si.tensor(shape, dtype, "w002", seed=31)
+    src_bufs = local_blocks(G, src)
+    want = oracle.reshard_fp8(shape, src, dst, src_bufs, dtype)
+    plan = make_plan(shape, ccl.DTYPES[dtype], src, dst)
+    try:
+        dsrc = upload_all(src_bufs, DEV)
+        codes = [DevBuf(w[0].size, DEV) for w in want]
+        scales = [DevBuf(w[1].nbytes, DEV) for w in want]
+        ccl.check(ccl.ccl_reshard_copy_fp8(plan, [b.ptr for b in dsrc], [b.ptr for b in codes],
+                                           [b.ptr for b in scales], torch.cuda.current_stream(),
+                                           ccl.LaunchConfig(**cfg)), "reshard_copy_fp8")
+        torch.cuda.synchronize()
+        for c, f, (wc, wf) in zip(codes, scales, want):
+            assert c.guards_intact() and f.guards_intact()
+            np.testing.assert_array_equal(f.download(np.float32).view(np.uint32), wf.view(np.uint32))
+            np.testing.assert_array_equal(c.download(np.uint8), wc)
     finally:
         ccl.check(ccl.ccl_plan_destroy(plan))
 

@@ -70,7 +70,8 @@ def test_bf16_hidden_16384_and_in_place():
 
 
 @pytest.mark.parametrize("cfg", [dict(workgroups=1), dict(workgroups=7), dict(occupancy=1),
-                                 dict(occupancy=32), dict(nontemporal=4)])
+                                 dict(occupancy=32), dict(nontemporal=1), dict(nontemporal=2),
+                                 dict(nontemporal=4)])
 def test_launch_config_does_not_change_results(cfg):
     P, rows, hidden = 8, 40, 4096
     xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=9)
