@@ -125,7 +125,8 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
 // staging kernel as future work, with no format.  This library's format: OCP
 // FP8 E4M3 (bias 7, largest finite 448, no infinities) with one fp32 scale
 // per block of 128 consecutive elements of each destination's local buffer;
-// scale = amax / 448 (1 for an all-zero block), code = round-to-nearest-even
+// scale = amax / 448 (1 when that is zero: an all-zero block, or an amax so
+// small that the quotient underflows), code = round-to-nearest-even
 // of x / scale, saturated at +-448.  The plan must place every block inside
 // one interval (checked on the host), so a group of lanes owns one block:
 // its lanes read the block's 16-byte vectors once, agree on amax through
@@ -153,46 +154,49 @@ struct ReshardFp8Args {
 // a quotient within one ulp, corrected once by its exact residual times the
 // correctly rounded reciprocal).  It needs the residuals to stay normal, which
 // holds for every quotient that can reach a nonzero code when
-// 2^-60 <= scale <= 2^64; the kernel divides outside that range.  A zero
-// quotient's sign is taken from x.
+// 2^-60 <= scale <= 2^64; the kernel divides outside that range.  The
+// residual is formed as scale * q - x and subtracted, which keeps the sign of
+// a zero quotient (x - scale * q would turn -0 into +0).
 __device__ __forceinline__ float quot_rcp(float x, float scale, float rcp) {
   float q = x * rcp;
-  float r = fmaf(-scale, q, x);
-  q = fmaf(r, rcp, q);
-  r = fmaf(-scale, q, x);
-  return copysignf(fmaf(r, rcp, q), x);
+  float r = fmaf(scale, q, -x);
+  q = fmaf(-r, rcp, q);
+  r = fmaf(scale, q, -x);
+  return fmaf(-r, rcp, q);
 }
 
 // Maximum over each aligned group of N (16 or 32) lanes, left in every lane
-// of the group; all 64 lanes must be active.  Within a 16-lane DPP row:
+// of the group; all 64 lanes must be active.  Values are the bit patterns of
+// non-negative floats, whose unsigned order is their numeric order.  Within a 16-lane DPP row:
 // swap neighbours, swap pairs (each lane now holds its quad's maximum), then
 // the row's half-mirror and full mirror pair every lane with a lane of the
 // other quad / other half.  A 32-lane group adds an exchange between its two
 // rows (swizzle with lane xor 16).
 template <int CTRL>
-__device__ __forceinline__ float dpp_max(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return fmaxf(v, __int_as_float(o));
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+  return v > o ? v : o;
 }
 template <int N>
-__device__ __forceinline__ float group_max(float v) {
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
   v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
   v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
   v = dpp_max<0x141>(v);  // row_half_mirror
   v = dpp_max<0x140>(v);  // row_mirror
-  if constexpr (N == 32)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+  if constexpr (N == 32) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+    v = v > o ? v : o;
+  }
   return v;
 }
 
 // Two quotients -> two E4M3 codes (OCP: bias 7, largest finite 448), round to
-// nearest even with subnormal codes, magnitudes above 448 saturated, packed
-// into the low (HI false) or high half of `word`.  gfx950's conversion
-// implements exactly this rounding on values already clamped to +-448.
+// nearest even with subnormal codes, packed into the low (HI false) or high
+// half of `word`.  gfx950's conversion implements exactly this rounding for
+// |y| < 464 (magnitudes in [448, 464) round to 448); larger ones must be
+// clamped to +-448 first.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t word) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)word, HI);
 }
 
@@ -236,7 +240,7 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
         const uint64_t v = v0 + (uint64_t)u * kThreads + threadIdx.x;
         const bool live = v < nvec;
         float x[EPL];
-        float amax = 0.f;
+        uint32_t amax_bits = 0;  // max |x| as a bit pattern (finite inputs)
         // a short last block: elements past the interval do not count
         const uint32_t valid = live ? (uint32_t)min<uint64_t>(EPL, (bytes - v * kVecBytes) / esz) : 0u;
         if (live) {
@@ -254,24 +258,33 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
           }
           if (valid == (uint32_t)EPL) {  // every vector but a chunk's last
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
+            for (int e = 0; e < EPL; ++e) {
+              const uint32_t m = __float_as_uint(x[e]) & 0x7fffffffu;
+              amax_bits = m > amax_bits ? m : amax_bits;
+            }
           } else {
 #pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              if ((uint32_t)e < valid) amax = fmaxf(amax, fabsf(x[e]));
+            for (int e = 0; e < EPL; ++e) {
+              const uint32_t m = __float_as_uint(x[e]) & 0x7fffffffu;
+              if ((uint32_t)e < valid && m > amax_bits) amax_bits = m;
+            }
           }
         }
-        amax = group_max<LPB>(amax);
+        const float amax = __uint_as_float(group_max<LPB>(amax_bits));
         if (!live) continue;  // every lane has taken part in this vector's shuffles
-        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        const float q448 = amax / 448.0f;
+        const float scale = q448 > 0.f ? q448 : 1.0f;
         float y[EPL];
         if (scale >= 0x1p-60f && scale <= 0x1p64f) {
+          // |x| <= amax and scale = amax / 448 within half an ulp: |y| < 449
           const float rcp = 1.0f / scale;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) y[e] = quot_rcp(x[e], scale, rcp);
         } else {
+          // a subnormal (or zero) scale loses the bound on |y|: clamp
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) y[e] = x[e] / scale;
+          for (int e = 0; e < EPL; ++e)
+            y[e] = __builtin_amdgcn_fmed3f(x[e] / scale, -448.0f, 448.0f);
         }
         const uint64_t e_off = v * EPL;  // element offset in the chunk's destination run
         const uint32_t lo = e4m3_pack2<true>(y[2], y[3], e4m3_pack2<false>(y[0], y[1], 0u));

@@ -77,7 +77,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
  *   reshard copy    32 KiB chunks, unroll 4, <= 2 WGs per CU
- *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
+ *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  one workgroup per row, residency bounded only by
  *                   registers and the row buffer it keeps in LDS; it reads
@@ -314,8 +314,9 @@ ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_buf
  * future work and fixes no format; this is the format chosen here).  Every
  * destination buffer is written as OCP FP8 E4M3 codes (1 byte per element,
  * bias 7, largest finite 448) plus one fp32 scale per block of 128
- * consecutive elements of its local buffer: scale = amax / 448 in fp32 (1 for
- * an all-zero block), code = round-to-nearest-even of x / scale in fp32,
+ * consecutive elements of its local buffer: scale = amax / 448 in fp32 (1 when
+ * that is zero: an all-zero block, or an amax so small that the quotient
+ * underflows), code = round-to-nearest-even of x / scale in fp32,
  * saturated to +-448.  Dequantize as code_value * scale.  Source elements
  * must be finite: a block holding a NaN or an infinity gets unspecified
  * codes and scale.

@@ -581,7 +581,8 @@ static unsigned e4m3_nearest_sat(float y) {
 
 /*
  * Quantize n elements in blocks of `block`: per block, amax = max |x| (fp32),
- * scale = amax / 448 in fp32 (1 when amax is 0), code = nearest E4M3 to
+ * scale = amax / 448 in fp32 (1 when that is 0: an all-zero block, or an amax
+ * so small that the quotient underflows), code = nearest E4M3 to
  * x / scale in fp32.  The M2N part of the digest (lqnn.cn news 207677) s1.5
  * names quantizing weights on the fly inside the staging kernel as future
  * work without fixing a format; this is the format this library picks.
@@ -597,7 +598,8 @@ int orc_quantize_e4m3(const void *x, int dtype, size_t n, size_t block, uint8_t 
             const float v = fabsf(load_as_f32(x, i, dtype));
             if (v > amax) amax = v;
         }
-        const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+        const float q = amax / 448.0f;
+        const float scale = q > 0.f ? q : 1.0f;
         scales[b0 / block] = scale;
         for (size_t i = b0; i < b1; ++i) codes[i] = (uint8_t)e4m3_nearest_sat(load_as_f32(x, i, dtype) / scale);
     }

@@ -9,6 +9,7 @@ query.
 """
 from __future__ import annotations
 
+import functools
 import gc
 
 import numpy as np
@@ -337,6 +338,15 @@ def _fp8_edge_blocks(dtype: str, rng) -> list:
     tiny = 2.0 ** -20 if f16 else 2.0 ** -130                               # subnormal inputs
     blocks.append(block([4 * tiny], rng.integers(-4, 5, 200) * tiny))
     if not f16:
+        # subnormal block maxima: amax / 448 rounds coarsely (or to 0 for fp32's
+        # smallest), so quotients can land well past 448 and must saturate
+        sub_maxima = [2.0 ** -133, 3 * 2.0 ** -133] + ([2.0 ** -149, 2.0 ** -140, 5 * 2.0 ** -146]
+                                                         if dtype == "f32" else [])
+        for amax in sub_maxima:
+            q = 2.0 ** -149 if dtype == "f32" else 2.0 ** -133
+            k = int(round(amax / q))
+            body = (rng.integers(-k, k + 1, 300) * q).astype(np.float32)
+            blocks.append(block([amax, -amax], body))
         for amax in (2.0 ** -70, 448 * 2.0 ** -60, 2.0 ** 80, 448 * 2.0 ** 64):
             a = np.float32(amax)
             lo = np.nextafter(a, np.float32(0)) if dtype == "f32" else a
@@ -379,15 +389,22 @@ def test_reshard_fp8_edge_values(dtype):
         ccl.check(ccl.ccl_plan_destroy(plan))
 
 
+@functools.lru_cache(maxsize=None)
+def _fp8_variant_case(dtype):
+    """Inputs and oracle outputs shared by every launch variant of one dtype."""
+    shape, src, dst = FP8_CASES[1]
+    G = si.tensor(shape, dtype, "w002", seed=31)
+    src_bufs = local_blocks(G, src)
+    return src_bufs, oracle.reshard_fp8(shape, src, dst, src_bufs, dtype)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("cfg", [dict(unroll=1), dict(unroll=4), dict(nontemporal=1),
                                  dict(nontemporal=2), dict(nontemporal=4, unroll=1),
                                  dict(chunk_bytes=1024, workgroups=3), dict(occupancy=2)])
 def test_reshard_fp8_launch_variants(cfg, dtype):
     shape, src, dst = FP8_CASES[1]
-    G = si.tensor(shape, dtype, "w002", seed=31)
-    src_bufs = local_blocks(G, src)
-    want = oracle.reshard_fp8(shape, src, dst, src_bufs, dtype)
+    src_bufs, want = _fp8_variant_case(dtype)
     plan = make_plan(shape, ccl.DTYPES[dtype], src, dst)
     try:
         dsrc = upload_all(src_bufs, DEV)

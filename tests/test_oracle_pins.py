@@ -544,3 +544,24 @@ def test_blockwise_quantization_round_trip_error_bound():
         assert np.isclose(np.max(np.abs(deq[sl])), amax, rtol=2 ** -4)
         err = np.abs(deq[sl] - xf[sl])
         assert np.all(err <= np.maximum(np.abs(xf[sl]) * 2 ** -4, scales[b] * 2.0 ** -10) * 1.0001)
+
+
+def test_quantization_scale_that_underflows_is_one():
+    """A block whose amax / 448 rounds to zero in fp32 (amax = 2^-149, the
+    smallest subnormal) is scaled like an all-zero block: scale 1, and every
+    element, far below E4M3's smallest step, codes to a signed zero.  A block
+    whose amax / 448 is a coarse subnormal keeps that scale, and its largest
+    elements saturate at 448 instead of overflowing."""
+    tiny = np.float32(2.0 ** -149)
+    x = np.array([tiny, 0.0, -tiny, -0.0] * 32, np.float32)
+    codes, scales = oracle.quantize_e4m3(x, "f32")
+    assert scales.view(np.uint32)[0] == np.float32(1.0).view(np.uint32)
+    assert list(codes[:4]) == [0x00, 0x00, 0x80, 0x80]
+    amax = np.float32(3 * 2.0 ** -140)
+    y = np.zeros(128, np.float32)
+    y[0], y[1] = amax, -amax
+    codes, scales = oracle.quantize_e4m3(y, "f32")
+    s = scales[0]
+    assert 0 < s < 2.0 ** -126 and s == np.float32(amax) / np.float32(448)
+    assert amax / np.float64(s) > 448           # the quotient overshoots 448 ...
+    assert codes[0] == 0x7E and codes[1] == 0xFE  # ... and saturates
