@@ -230,6 +230,12 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
       if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
     }
   }
+  // Default residency by row length: rows of 4-8 KiB per rank run best with at
+  // most 3 workgroups per CU, shorter and longer ones uncapped.
+  if (!cfg || cfg->occupancy == 0) {
+    const uint64_t row_bytes = hidden * sz;
+    l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+  }
   ccl::RmsDesc d{nranks, dtype, rows, hidden, eps, send, recv, gamma};
   return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream);
 }

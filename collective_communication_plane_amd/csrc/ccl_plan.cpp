@@ -34,8 +34,7 @@ struct Layout {
   int64_t parts;          // blocks along shard_dim (1 if replicated)
 };
 
-ccl_status_t make_layout(const ccl_mesh_t *m, const ccl_placement_t *pl, int ndim,
-                         const int64_t *shape, Layout *L) {
+ccl_status_t make_layout(const ccl_mesh_t *m, const ccl_placement_t *pl, int ndim, Layout *L) {
   if (!m || !pl) return CCL_ERR_INVALID_ARG;
   if (m->ndims < 1 || m->ndims > CCL_MAX_MESH_DIMS || m->start_rank < 0)
     return CCL_ERR_INVALID_ARG;
@@ -122,8 +121,8 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
   const int64_t *shape = tensor->shape;
   Layout S, D;
   ccl_status_t st;
-  if ((st = make_layout(src_mesh, src_placements, ndim, shape, &S))) return st;
-  if ((st = make_layout(dst_mesh, dst_placements, ndim, shape, &D))) return st;
+  if ((st = make_layout(src_mesh, src_placements, ndim, &S))) return st;
+  if ((st = make_layout(dst_mesh, dst_placements, ndim, &D))) return st;
   // The two meshes must be disjoint rank ranges.
   if (!(S.start + S.size <= D.start || D.start + D.size <= S.start)) return CCL_ERR_LAYOUT;
 

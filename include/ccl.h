@@ -79,9 +79,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   reshard copy    32 KiB chunks, unroll 4, <= 2 WGs per CU
  *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
- *   all-reduce + RMSNorm  one workgroup per row, residency bounded only by
- *                   registers and the row buffer it keeps in LDS; it reads
- *                   workgroups, nontemporal and occupancy and ignores the rest
+ *   all-reduce + RMSNorm  one workgroup per row; <= 3 WGs per CU for rows of
+ *                   4-8 KiB, otherwise residency bounded only by registers and
+ *                   the row buffer it keeps in LDS; it reads workgroups,
+ *                   nontemporal and occupancy and ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
  * use a register-direct kernel that realigns the inputs in VGPRs.
  * A zero field means "the default for this call"; out-of-range values give
