@@ -302,8 +302,11 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
  *   dst_bufs   one pointer per destination-mesh rank, likewise.
  *   Any overlap of two destination buffers, or of a source and a
  *   destination buffer, gives CCL_ERR_ALIASING.
- * The first call on a device copies the plan's interval table to device
- * memory (stream-ordered, then cached in the plan until ccl_plan_destroy).
+ * The first call for a device and chunk size allocates device memory for the
+ * plan's interval table and copies it there synchronously (hipMalloc, then
+ * blocking hipMemcpy); later calls reuse it until ccl_plan_destroy.  So make
+ * that first call outside stream capture.  The same holds for
+ * ccl_reshard_copy_fp8, whose chunks are rounded to whole 128-element blocks.
  */
 ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_bufs,
                               void *const *dst_bufs, void *stream,
