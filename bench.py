@@ -32,6 +32,8 @@ Other modes:
   --calibrate   also runs a plain 1 GiB device copy (torch) a few times, the
                 known-size reference that scales rocprofv3's FETCH_SIZE and
                 WRITE_SIZE counters to bytes.
+  --sizes       all-reduce at P = 8 over per-rank sizes 4 KiB ... 1 GiB (x4 steps),
+                fp32 and bf16, sum / min / max: per-call median / min / max.
   --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
                 16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
                 same kernel), with the default and an uncapped occupancy, next
@@ -103,6 +105,47 @@ def timed(launch, steps: int, warmup: int, stream, min_warm_s: float = 0.0):
     return start.elapsed_time(stop) / steps  # ms per launch
 
 
+def per_call_stats(launch, stream, repeats: int = 20, min_repeat_ms: float = 2.0):
+    """Median, min and max ms per call over `repeats` timed batches of K
+    back-to-back calls, K chosen so that one batch takes at least
+    `min_repeat_ms`."""
+    import statistics
+
+    import torch
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    launch()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    k = max(1, int(min_repeat_ms / max(t0.elapsed_time(t1), 1e-3)) + 1)
+    per_call = []
+    for _ in range(repeats):
+        t0.record(stream)
+        for _ in range(k):
+            launch()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per_call.append(t0.elapsed_time(t1) / k)
+    return {"median": round(statistics.median(per_call), 5), "min": round(min(per_call), 5),
+            "max": round(max(per_call), 5), "repeats": repeats, "calls_per_repeat": k}
+
+
+def device_copy_gbs(dev, stream) -> float:
+    """A plain 1 GiB device-to-device copy (torch copy_, the runtime's copy
+    kernel), as context for what one read and one write stream reach."""
+    import torch
+
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    ms = timed(lambda: dst.copy_(src), 20, 10, stream, 0.3)
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+
+
 def up(a, dev):
     import numpy as np
     import torch
@@ -130,8 +173,23 @@ def rank_slab(P: int, nbytes: int, dev, gap: int = RANK_GAP):
     return [slab[r * stride:r * stride + nbytes] for r in range(P)], stride
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float = 10.0):
-    """The oracle on a bounded sample: 8 ranks x 2^22 bf16 (8 MiB each)."""
+    """The oracle on a bounded sample: 8 ranks x 2^22 bf16 (8 MiB each), on
+    one thread and on every host core available to this process (up to 16),
+    each thread running the same oracle call on its own contiguous slice of
+    the elements (ctypes releases the GIL during the call)."""
+    import threading
+
     import numpy as np
 
     import oracle
@@ -139,19 +197,35 @@ def cpu_baseline(seconds: float = 10.0):
 
     P, n = 8, 1 << 22
     xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.all_reduce(xs, "bf16", "sum")
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    gbs = reps * 2 * P * n * 2 / el / 1e9
-    del np
-    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+
+    def run(T: int, budget: float):
+        bounds = [n * t // T for t in range(T + 1)]
+        parts = [[np.ascontiguousarray(x[bounds[t]:bounds[t + 1]]) for x in xs] for t in range(T)]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            th = [threading.Thread(target=oracle.all_reduce, args=(parts[t], "bf16", "sum"))
+                  for t in range(T)]
+            for t in th:
+                t.start()
+            for t in th:
+                t.join()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps * 2 * P * n * 2 / el / 1e9, reps, el
+
+    try:
+        T = min(16, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        T = min(16, os.cpu_count() or 1)
+    one, reps1, el1 = run(1, seconds / 2)
+    many, repsT, elT = run(T, seconds / 2)
+    return {"value": round(many, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "single_thread_value": round(one, 3),
             "sample": f"all_reduce sum over 8 ranks x 4,194,304 bf16 (first 8 MiB of the "
-                      f"workload's shape, same distribution), {reps} repetitions in {el:.1f} s, "
-                      f"one thread"}
+                      f"workload's shape, same distribution): {repsT} repetitions in {elT:.1f} s "
+                      f"on {T} threads, each running the oracle on its own slice; "
+                      f"{reps1} repetitions in {el1:.1f} s on one thread; CPU {_cpu_model()}"}
 
 
 def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
@@ -342,6 +416,39 @@ def streams(dev, stream) -> None:
         torch.cuda.empty_cache()
 
 
+def sizes(dev, stream) -> None:
+    """All-reduce at P=8 over per-rank sizes 4 KiB * 4^k (k = 0..9, up to 1 GiB),
+    fp32 and bf16, sum / min / max, library defaults, ranks in staggered slabs;
+    per-call median / min / max over 20 repeats.  One JSON line per point."""
+    import torch
+
+    from collective_communication_plane_amd import ccl
+
+    P = 8
+    codes = {"bf16": (ccl.CCL_BFLOAT16, torch.bfloat16, 2), "f32": (ccl.CCL_FLOAT32, torch.float32, 4)}
+    ops = {"sum": ccl.CCL_SUM, "min": ccl.CCL_MIN, "max": ccl.CCL_MAX}
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    for k in range(10):
+        nbytes = 4096 * 4 ** k
+        dx, _ = rank_slab(P, nbytes, dev)
+        dy, _ = rank_slab(P, nbytes, dev)
+        for dt, (code, tdt, esz) in codes.items():
+            n = nbytes // esz
+            for d in dx:
+                d.view(tdt).copy_(torch.rand(n, generator=g, device=dev).mul_(2).sub_(1))
+            for opn, op in ops.items():
+                st = per_call_stats(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, code, op, stream)),
+                                    stream)
+                gbs = 2 * P * nbytes / (st["median"] * 1e-3) / 1e9
+                print(json.dumps({"sizes": "all_reduce", "dtype": dt, "op": opn,
+                                  "bytes_per_rank": nbytes, "ms_per_call": st,
+                                  "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "cache_resident": 2 * P * nbytes <= (256 << 20)}), flush=True)
+        del dx, dy
+        torch.cuda.empty_cache()
+
+
 def calibrate(dev) -> None:
     """A plain 1 GiB device-to-device copy (reads 1 GiB, writes 1 GiB)."""
     import torch
@@ -366,9 +473,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true")
     ap.add_argument("--row-steps", type=int, default=50)
+    ap.add_argument("--row-warm-s", type=float, default=0.5,
+                    help="minimum warmup time per row (shorter under a counter profiler)")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--streams", action="store_true")
+    ap.add_argument("--sizes", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -393,6 +503,9 @@ def main() -> int:
         return 0
     if args.streams:
         streams(dev, stream)
+        return 0
+    if args.sizes:
+        sizes(dev, stream)
         return 0
     if args.calibrate:
         calibrate(dev)
@@ -423,6 +536,12 @@ def main() -> int:
     parity = bool(np.array_equal(got, want))
     del xs
 
+    per_call = per_call_stats(step, stream)
+    algbw = n * 2 / (ms * 1e-3) / 1e9  # per-rank message bytes / time
+    del dx, dy
+    torch.cuda.empty_cache()
+    copy_gbs = device_copy_gbs(dev, stream)
+
     traffic = read_traffic(bytes_per_step)
     line = {
         "metric": METRIC,
@@ -446,16 +565,18 @@ def main() -> int:
             "placement": f"each side one allocation, rank r at r x {stride} bytes "
                          f"(256 MiB + 2 MiB + 4 KiB apart)",
             "parity_spot_check": parity,
+            "per_call_ms": per_call,
+            "algbw_GBs": round(algbw, 1),
+            "busbw_GBs": round(algbw * 2 * (P - 1) / P, 1),
+            "device_copy_1GiB_GBs": copy_gbs,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
         },
     }
-    del dx, dy
-    torch.cuda.empty_cache()
     if not args.no_rows:
-        line["rows"] = rows(dev, stream, args.row_steps, 5)
+        line["rows"] = rows(dev, stream, args.row_steps, 5, args.row_warm_s)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

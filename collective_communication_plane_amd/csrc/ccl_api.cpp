@@ -72,6 +72,7 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
           cfg->chunk_bytes > (uint64_t(1) << 32))
         return CCL_ERR_INVALID_ARG;
       l.chunk_bytes = cfg->chunk_bytes;
+      l.chunk_set = true;
     }
     if (cfg->workgroups < 0 || cfg->workgroups > (1 << 24)) return CCL_ERR_INVALID_ARG;
     l.workgroups = cfg->workgroups;
@@ -90,7 +91,10 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
       l.nt_store = (cfg->nontemporal >> 1) & 1;
     }
     if (cfg->occupancy < 0 || cfg->occupancy > 32 || cfg->reserved != 0) return CCL_ERR_INVALID_ARG;
-    if (cfg->occupancy) l.occupancy = cfg->occupancy;
+    if (cfg->occupancy) {
+      l.occupancy = cfg->occupancy;
+      l.occupancy_set = true;
+    }
   }
   if ((op == OP_RESHARD || op == OP_RESHARD_FP8) && explicit_stages && l.stages != 1)
     return CCL_ERR_UNSUPPORTED;
@@ -232,7 +236,7 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
   }
   // Default residency by row length: rows of 4-8 KiB per rank run best with at
   // most 3 workgroups per CU, shorter and longer ones uncapped.
-  if (!cfg || cfg->occupancy == 0) {
+  if (!l.occupancy_set) {
     const uint64_t row_bytes = hidden * sz;
     l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
   }

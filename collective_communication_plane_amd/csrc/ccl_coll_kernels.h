@@ -130,10 +130,23 @@ __device__ __forceinline__ void scalar_element(const CollArgs &a, int s, uint64_
   }
 }
 
+// Waves per SIMD the register-direct kernel must leave room for, from the
+// VGPRs its in-flight loads need (U x inputs x 4).  Without a target the
+// register allocator sometimes takes nearly all 256 VGPRs for a small body
+// (fp32 / fp16 / int32 all-reduce at P = 8, U = 1: 239 VGPRs plus 32 AGPRs of
+// copies), which leaves one wave per SIMD and a third of the bandwidth.
+template <int KIND, int PMAX, int U>
+struct VecWaves {
+  static constexpr int loads = U * (KIND == KIND_AG ? 1 : PMAX) * 4;
+  static constexpr int value = loads <= 64 ? 4 : loads <= 160 ? 2 : 1;
+};
+
 // Register-direct kernel.  PMAX bounds P at compile time so every load of a
 // lane's U x P vectors is issued before the first fold.
 template <int KIND, int DT, int OP, int PMAX, int U>
-__global__ void __launch_bounds__(kThreads) coll_vec_kernel(CollArgs a) {
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(VecWaves<KIND, PMAX, U>::value)))
+    coll_vec_kernel(CollArgs a) {
   constexpr int esz = (DT == CCL_BFLOAT16 || DT == CCL_FLOAT16) ? 2 : 4;
   constexpr int V = kVecBytes / esz;  // elements per vector
   constexpr int NI = KIND == KIND_AG ? 1 : PMAX;
@@ -165,21 +178,26 @@ __global__ void __launch_bounds__(kThreads) coll_vec_kernel(CollArgs a) {
 #pragma unroll
     for (int q = 0; q < NO; ++q) ob[q] = q < no ? out_at<KIND>(a, s, q, head, esz) : nullptr;
 
+#pragma unroll 1  // U alone sets the vectors per rank a lane has in flight
     for (uint64_t v = v0 + threadIdx.x; v < v1; v += (uint64_t)kThreads * U) {
+      // Every element of x is assigned on every path (zero where there is no
+      // rank or no vector), so no value has to survive from the previous
+      // iteration; otherwise the compiler carries all of them along and the
+      // small fp32 / int32 bodies took ~240 VGPRs (one wave per SIMD).
       u32x4 x[U][NI];
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t vv = v + (uint64_t)u * kThreads;
-        if (vv < v1) {
-          if (ntl) {
+        const bool live = vv < v1;
+        if (ntl) {
 #pragma unroll
-            for (int r = 0; r < NI; ++r)
-              if (r < ni) x[u][r] = ld_nt(ib[r] + vv * kVecBytes);
-          } else {
+          for (int r = 0; r < NI; ++r)
+            x[u][r] = (live && r < ni) ? ld_nt(ib[r] + vv * kVecBytes) : zero;
+        } else {
 #pragma unroll
-            for (int r = 0; r < NI; ++r)
-              if (r < ni) x[u][r] = ld_plain(ib[r] + vv * kVecBytes);
-          }
+          for (int r = 0; r < NI; ++r)
+            x[u][r] = (live && r < ni) ? ld_plain(ib[r] + vv * kVecBytes) : zero;
         }
       }
 #pragma unroll

@@ -32,7 +32,10 @@ enum Op { OP_AR = 0, OP_RS = 1, OP_AG = 2, OP_RESHARD = 3, OP_RMSNORM = 4, OP_RE
 inline OpDefaults default_launch(Op op, int P) {
   switch (op) {
     case OP_AR:
-      return P <= 2 ? OpDefaults{8192, 1, 2, 8} : OpDefaults{4096, 1, 1, 3};
+      if (P == 1) return {8192, 1, 1, 8};
+      if (P == 2) return {8192, 1, 2, 8};
+      if (P <= 4) return {4096, 1, 1, 6};
+      return {4096, 1, 1, 3};
     case OP_RS:
       if (P <= 2) return {8192, 1, 2, 4};
       if (P >= 7 && P <= 12) return {8192, 2, 2, 2};
@@ -72,6 +75,8 @@ struct Launch {
   bool nt_load;
   bool nt_store;
   int occupancy;   // max resident workgroups per CU, 0 = no cap
+  bool chunk_set = false;      // chunk_bytes came from the caller
+  bool occupancy_set = false;  // occupancy came from the caller
 };
 
 // Dynamic LDS to request so that at most `occupancy` workgroups fit on a CU

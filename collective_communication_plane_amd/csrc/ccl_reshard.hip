@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(kThreads) reshard_kernel(ReshardArgs a) {
 #pragma unroll
       for (int u = 0; u < kReshardUnroll; ++u) {
         const uint64_t vv = v + (uint64_t)u * kThreads;
-        if (vv < nvec) x[u] = ld<NTL>(vs + vv * kVecBytes);
+        x[u] = vv < nvec ? ld<NTL>(vs + vv * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
       }
       for (int j = 0; j < a.rho; ++j) {
         char *d = a.dst[rep[j]] + dst_base + head;
@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint64_t v = v0 + (uint64_t)u * kThreads + threadIdx.x;
-        if (v < nvec) w[u] = ld<NTL>(src + v * kVecBytes);
+        w[u] = v < nvec ? ld<NTL>(src + v * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -99,10 +99,7 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
       u32x4 x[PMAX];
 #pragma unroll
       for (int r = 0; r < PMAX; ++r)
-        if (r < P) {
-          const char *p = a.in[r] + base + (uint64_t)v * kVecBytes;
-          x[r] = ld<NTL>(p);
-        }
+        x[r] = r < P ? ld<NTL>(a.in[r] + base + (uint64_t)v * kVecBytes) : u32x4{0u, 0u, 0u, 0u};
       const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
       row_buf[v] = sv;
       float f[8];

@@ -68,8 +68,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
  * configuration is tuned by a sweep).  Pass NULL for the built-in defaults,
  * which come from that sweep on MI355X (2 GiB of bf16 input over P ranks):
- *   all-reduce      P <= 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
- *                   P >= 3: 4 KiB chunks, unroll 1, <= 3 WGs per CU
+ *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
+ *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
+ *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU;
+ *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU
  *   reduce-scatter  7 <= P <= 12: LDS pipeline, 2 stages, 8 KiB chunks,
  *                   <= 2 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2) or 3 WGs per CU
@@ -84,7 +86,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   the row buffer it keeps in LDS; it reads workgroups,
  *                   nontemporal and occupancy and ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
- * use a register-direct kernel that realigns the inputs in VGPRs.
+ * use a register-direct kernel that realigns the inputs in VGPRs; unless the
+ * caller sets them, it runs 4 KiB chunks with <= 8 WGs per CU (all-gather:
+ * <= 4 for P <= 6, <= 3 above).
  * A zero field means "the default for this call"; out-of-range values give
  * CCL_ERR_INVALID_ARG.  None of these fields changes any result.
  *
