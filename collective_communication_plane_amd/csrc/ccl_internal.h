@@ -38,7 +38,6 @@ inline OpDefaults default_launch(Op op, int P) {
       return {4096, 1, 1, 3};
     case OP_RS:
       if (P <= 2) return {8192, 1, 2, 4};
-      if (P >= 7 && P <= 12) return {8192, 2, 2, 2};
       return {8192, 1, 2, 3};
     case OP_AG:
       if (P <= 2) return {8192, 1, 2, 4};
@@ -76,6 +75,7 @@ struct Launch {
   bool nt_store;
   int occupancy;   // max resident workgroups per CU, 0 = no cap
   bool chunk_set = false;      // chunk_bytes came from the caller
+  bool stages_set = false;     // stages came from the caller
   bool occupancy_set = false;  // occupancy came from the caller
 };
 

@@ -72,9 +72,11 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU;
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU
- *   reduce-scatter  7 <= P <= 12: LDS pipeline, 2 stages, 8 KiB chunks,
- *                   <= 2 WGs per CU; otherwise register-direct, 8 KiB chunks,
- *                   unroll 2, <= 4 (P <= 2) or 3 WGs per CU
+ *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
+ *                   <= 4 (P <= 2) or 3 WGs per CU; for 7 <= P <= 12 with more
+ *                   than 160 MiB per rank, the 2-stage LDS pipeline with <= 2
+ *                   WGs per CU
+ *   broadcast       as all-gather
  *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
