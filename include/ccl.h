@@ -47,7 +47,7 @@ extern "C" {
 typedef enum {
     CCL_OK = 0,
     CCL_ERR_INVALID_ARG = 1, /* NULL pointer, bad count/P/dtype/op, misaligned pointer */
-    CCL_ERR_UNSUPPORTED = 2, /* valid request this build does not implement */
+    CCL_ERR_UNSUPPORTED = 2, /* a valid request the library does not implement */
     CCL_ERR_ALIASING = 3,    /* buffers overlap in a way the op cannot run in place */
     CCL_ERR_LAYOUT = 4,      /* reshard layout violates a constraint */
     CCL_ERR_HIP = 5,         /* a HIP runtime call failed */
