@@ -533,3 +533,35 @@ def test_reduce_and_broadcast_reject_bad_arguments():
     torch.cuda.synchronize()
     for b in bufs:
         assert (b.base == b.fill).all().item()
+
+
+def test_zero_length_calls_touch_nothing():
+    """count 0 / rows 0 / an empty tensor: every entry point returns CCL_OK and
+    leaves the (canary-filled) buffers as they were."""
+    P = 4
+    bufs = [DevBuf(256, DEV) for _ in range(2 * P)]
+    send, recv = [b.ptr for b in bufs[:P]], [b.ptr for b in bufs[P:]]
+    gamma = DevBuf(64, DEV)
+    stream = torch.cuda.current_stream()
+    for dt in (ccl.CCL_FLOAT32, ccl.CCL_BFLOAT16, ccl.CCL_INT32, ccl.CCL_FLOAT16):
+        assert ccl.ccl_all_reduce(send, recv, P, 0, dt, ccl.CCL_SUM, stream) == ccl.CCL_OK
+        assert ccl.ccl_reduce_scatter(send, recv, P, 0, dt, ccl.CCL_MAX, stream) == ccl.CCL_OK
+        assert ccl.ccl_all_gather(send, recv, P, 0, dt, stream) == ccl.CCL_OK
+        assert ccl.ccl_reduce(send, recv[0], P, 0, dt, ccl.CCL_MIN, 1, stream) == ccl.CCL_OK
+        assert ccl.ccl_broadcast(send[0], recv, P, 0, dt, 2, stream) == ccl.CCL_OK
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, 0, 64, gamma.ptr, 1e-6, ccl.CCL_BFLOAT16,
+                                      stream) == ccl.CCL_OK
+    desc = ccl.make_tensor_desc((0, 64), ccl.CCL_BFLOAT16)
+    st, plan = ccl.ccl_reshard_plan(desc, ccl.make_mesh([2], 0), ccl.make_placements([("S", 1)]),
+                                    ccl.make_mesh([2], 2), ccl.make_placements(["R"]))
+    ccl.check(st, "reshard_plan")
+    try:
+        assert ccl.ccl_reshard_copy(plan, send[:2], recv[:2], stream) == ccl.CCL_OK
+        assert ccl.ccl_reshard_copy_fp8(plan, send[:2], recv[:2], [gamma.ptr, gamma.ptr + 32],
+                                        stream) == ccl.CCL_OK
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+    torch.cuda.synchronize()
+    for b in bufs + [gamma]:
+        assert b.guards_intact()
+        assert bool((b.base == b.fill).all().item()), "a zero-length call wrote"
