@@ -33,7 +33,9 @@ Other modes:
                 known-size reference that scales rocprofv3's FETCH_SIZE and
                 WRITE_SIZE counters to bytes.
   --sizes       all-reduce at P = 8 over per-rank sizes 4 KiB ... 1 GiB (x4 steps),
-                fp32 and bf16, sum / min / max: per-call median / min / max.
+                fp32 and bf16, sum / min / max: per-call median / min / max of
+                host-issued calls, and the per-call median of 20 calls replayed
+                from one HIP graph (no host work per call).
   --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
                 16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
                 same kernel), with the default and an uncapped occupancy, next
@@ -130,6 +132,39 @@ def per_call_stats(launch, stream, repeats: int = 20, min_repeat_ms: float = 2.0
         per_call.append(t0.elapsed_time(t1) / k)
     return {"median": round(statistics.median(per_call), 5), "min": round(min(per_call), 5),
             "max": round(max(per_call), 5), "repeats": repeats, "calls_per_repeat": k}
+
+
+def graph_per_call_ms(launch, calls: int = 20, repeats: int = 20) -> float:
+    """Median ms per call of `calls` launches captured in one HIP graph and
+    replayed `repeats` times (no host work per call)."""
+    import statistics
+
+    import torch
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch(s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            launch(torch.cuda.current_stream())
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    per = []
+    for _ in range(repeats):
+        t0.record(cur)
+        g.replay()
+        t1.record(cur)
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) / calls)
+    del g
+    return statistics.median(per)
 
 
 def device_copy_gbs(dev, stream) -> float:
@@ -441,9 +476,14 @@ def sizes(dev, stream) -> None:
                 st = per_call_stats(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, code, op, stream)),
                                     stream)
                 gbs = 2 * P * nbytes / (st["median"] * 1e-3) / 1e9
+                gms = graph_per_call_ms(
+                    lambda s: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, code, op, s)))
+                ggbs = 2 * P * nbytes / (gms * 1e-3) / 1e9
                 print(json.dumps({"sizes": "all_reduce", "dtype": dt, "op": opn,
                                   "bytes_per_rank": nbytes, "ms_per_call": st,
                                   "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "graph_ms_per_call": round(gms, 5),
+                                  "graph_GB/s": round(ggbs, 1),
                                   "cache_resident": 2 * P * nbytes <= (256 << 20)}), flush=True)
         del dx, dy
         torch.cuda.empty_cache()
