@@ -352,14 +352,27 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
         tensor_bytes = sum(t.numel() for t in dsrc)
         dbytes = tensor_bytes * rho // ndst
         ddst = [torch.empty(dbytes, dtype=torch.uint8, device=dev) for _ in range(ndst)]
-        st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
-                                        ccl.make_mesh(src[0], src[1]), ccl.make_placements(src[2]),
-                                        ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))
+        args = (ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
+                ccl.make_mesh(src[0], src[1]), ccl.make_placements(src[2]),
+                ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))
+        # host planning time: median of 20 plans of the same layouts
+        plan_us = []
+        for _ in range(20):
+            t0 = time.perf_counter()
+            st, p = ccl.ccl_reshard_plan(*args)
+            plan_us.append((time.perf_counter() - t0) * 1e6)
+            ccl.check(st, "reshard_plan")
+            ccl.check(ccl.ccl_plan_destroy(p))
+        st, plan = ccl.ccl_reshard_plan(*args)
         ccl.check(st, "reshard_plan")
+        st, n_iv = ccl.ccl_plan_num_intervals(plan)
+        ccl.check(st, "plan_num_intervals")
         ms = timed(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream)), steps,
                    warmup, stream, warm_s)
         record(name, tensor_bytes * (1 + rho), ms,
                f"reshard {list(shape)} bf16 {src} -> {dst}")
+        out[name]["plan_host_us"] = round(sorted(plan_us)[len(plan_us) // 2], 1)
+        out[name]["plan_intervals"] = n_iv
         if name == "reshard_weight":
             # the same reshard, quantized to FP8 E4M3 with 128-element scales while staged
             n_local = dbytes // 2
