@@ -135,6 +135,32 @@ def test_ar_p8_256mib_bf16_headline():
     print("non-bit-equal:", _ar_sampled(dx, P, n, "bf16", "sum", host_inputs=xs))
 
 
+def test_ar_p8_256mib_bf16_headline_in_bench_layout():
+    """The headline workload in the buffer layout the benchmark times: inputs and
+    outputs as byte views into one allocation each, 2 MiB + 4 KiB apart."""
+    import bench
+
+    P, n = 8, 134_217_728
+    xs = si.rank_buffers(P, n, "bf16", "uniform", seed=0)
+    dx, stride = bench.rank_slab(P, 2 * n, DEV)
+    dy, _ = bench.rank_slab(P, 2 * n, DEV)
+    assert stride % 256 == 0 and stride >= 2 * n + bench.RANK_GAP
+    for d, x in zip(dx, xs):
+        d.copy_(torch.from_numpy(np.ascontiguousarray(x).view(np.uint8)))
+    ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                 torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    for q in range(1, P):
+        assert torch.equal(dy[q], dy[0]), q
+    idx = si.sample_indices(n, 200_000, seed=11)
+    want = oracle.fold_at(xs, "bf16", "sum", idx)
+    got = gather_at([dy[0]], idx, "bf16")[0]
+    assert_parity(got, want, "bf16", "sum", "AR headline, bench layout")
+    # the inputs were not written
+    for d, x in zip(dx, xs):
+        assert torch.equal(d[:1 << 20].cpu(), torch.from_numpy(x.view(np.uint8)[:1 << 20].copy()))
+
+
 SWEEP_BYTES = [4096 * 4 ** k for k in range(10)]  # 4 KiB .. 1 GiB per rank
 
 
