@@ -287,3 +287,17 @@ def test_planner_empty_tensor():
         assert ccl.ccl_reshard_copy(plan, [0, 0], [0, 0]) == ccl.CCL_OK
     finally:
         ccl.ccl_plan_destroy(plan)
+
+
+def test_plain_c_client(tmp_path):
+    """include/ccl.h compiles as strict C99 and the library's host paths work
+    from C alone (tests/c_abi_client.c: status strings, early rejections, the
+    planner on Example A)."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    libdir = os.path.dirname(ccl.lib_path())
+    exe = str(tmp_path / "c_abi_client")
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                    "-I", os.path.dirname(HEADER), os.path.join(here, "c_abi_client.c"),
+                    "-L", libdir, "-lccl", f"-Wl,-rpath,{libdir}", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
