@@ -313,13 +313,20 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     record("all_reduce_bf16_allocator_placement", 2 * P * n * 2, ms,
            "all_reduce sum, P=8 x 134,217,728 bf16, library defaults, one torch tensor per "
            "rank buffer (the caching allocator's placement)")
-    lds_cfg = ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=2)
-    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+    # the LDS pipeline on the headline's buffer layout (staggered slabs), so
+    # that it compares with the headline's register-direct kernel
+    sx, _ = rank_slab(P, 2 * n, dev)
+    for d, t in zip(sx, dx):
+        d.copy_(t.view(torch.uint8))
+    del dx, dy
+    sy, _ = rank_slab(P, 2 * n, dev)
+    lds_cfg = ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=3)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(sx, sy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
                                                     stream, lds_cfg)), steps, warmup, stream, warm_s)
     record("all_reduce_bf16_lds_pipeline", 2 * P * n * 2, ms,
            "all_reduce sum, P=8 x 134,217,728 bf16, LDS pipeline (2 stages, 4 KiB chunks, "
-           "<= 2 workgroups per CU)")
-    del dx, dy
+           "<= 3 workgroups per CU), ranks in staggered slabs as in the headline")
+    del sx, sy
     torch.cuda.empty_cache()
 
     # all-reduce with RMSNorm fused between its halves: 16384 tokens x 8192 hidden
