@@ -141,3 +141,46 @@ def test_all_reduce_rmsnorm_past_4gib_per_rank():
     want = oracle.all_reduce_rmsnorm(xin, pick.size, hidden, gamma, 1e-6, "bf16")
     for q in range(P):
         assert_rmsnorm_parity(gather(dy[q], idx), want[q], "bf16", hidden, f"rank {q}")
+
+
+@pytest.mark.parametrize("P", [7, 8, 12])
+def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
+    """At 7 <= P <= 12 reduce-scatter and reduce switch from the register-direct
+    kernel to the LDS pipeline past 160 MiB per rank; both sides of that
+    switch must give the oracle's values (sum, sampled)."""
+    TORCH = {"bf16": torch.int16, "f32": torch.int32}
+    for dtype, per_rank_mib in (("bf16", 144), ("bf16", 176), ("f32", 168)):
+        esz = 2 if dtype == "bf16" else 4
+        # shard lengths of whole 16-byte vectors keep every shard aligned, so
+        # the aligned kernels (not the realigning one) run on both sides
+        M = (per_rank_mib << 20) // esz // P // 8 * 8 + 8
+        assert (P * M * esz > (160 << 20)) == (per_rank_mib > 160)
+        dx = si.device_rank_buffers(P, P * M, dtype, "normal", seed=P, device=DEV)
+        dy = [torch.empty(M, dtype=dx[0].dtype, device=DEV) for _ in range(P)]
+        code = ccl.CCL_BFLOAT16 if dtype == "bf16" else ccl.CCL_FLOAT32
+        ccl.check(ccl.ccl_reduce_scatter(dx, dy, P, M, code, ccl.CCL_SUM,
+                                         torch.cuda.current_stream()), "reduce_scatter")
+        red = torch.empty(P * M, dtype=dx[0].dtype, device=DEV)
+        ccl.check(ccl.ccl_reduce(dx, red, P, P * M, code, ccl.CCL_SUM, P - 1,
+                                 torch.cuda.current_stream()), "reduce")
+        torch.cuda.synchronize()
+        idx = samples(M, k=20_000, seed=P)
+        npdt = np.uint16 if dtype == "bf16" else np.uint32
+
+        def at(t, i):
+            it = torch.from_numpy(i).to(DEV)
+            return t.view(TORCH[dtype])[it].cpu().numpy().view(npdt)
+
+        for s in (0, P // 2, P - 1):
+            xin = [at(t, idx + s * M) for t in dx]
+            if dtype == "f32":
+                xin = [x.view(np.float32) for x in xin]
+            want = oracle.all_reduce(xin, dtype, "sum")[0]
+            got = at(dy[s], idx)
+            got_red = at(red, idx + s * M)
+            if dtype == "f32":
+                got, got_red = got.view(np.float32), got_red.view(np.float32)
+            assert_parity(got, want, dtype, "sum", f"RS P={P} {dtype} {per_rank_mib} MiB shard {s}")
+            assert_parity(got_red, want, dtype, "sum", f"reduce P={P} {dtype} {per_rank_mib} MiB")
+        del dx, dy, red
+        torch.cuda.empty_cache()
