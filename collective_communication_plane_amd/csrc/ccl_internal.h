@@ -77,6 +77,7 @@ struct Launch {
   bool chunk_set = false;      // chunk_bytes came from the caller
   bool stages_set = false;     // stages came from the caller
   bool occupancy_set = false;  // occupancy came from the caller
+  bool nt_set = false;         // nontemporal hints came from the caller
 };
 
 // Dynamic LDS to request so that at most `occupancy` workgroups fit on a CU

@@ -80,7 +80,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
  *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
  *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
- *   reshard copy    32 KiB chunks, unroll 4, <= 2 WGs per CU
+ *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
+ *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
+ *                   two or more: 32 KiB chunks, <= 2 WGs per CU,
+ *                   nontemporal stores only
  *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  one workgroup per row; <= 3 WGs per CU for rows of
@@ -111,7 +114,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                flight per rank (1, 2 or 4; 4 is used as 2 when P > 8); for
  *                the fp8 reshard, vectors each lane loads before quantizing.
  *   nontemporal  bit 0: nontemporal loads, bit 1: nontemporal stores;
- *                0 = default (both), 4 = neither.
+ *                0 = default (both; stores only for a reshard copy with
+ *                replicated destinations), 4 = neither.
  *   occupancy    at most this many workgroups resident per compute unit
  *                (enforced by reserving LDS), 1..32; 32 is effectively no
  *                cap.  Fewer resident waves keep fewer DRAM pages open at
