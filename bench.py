@@ -300,7 +300,17 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     ms = timed(lambda: ccl.check(ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, stream)),
                steps, warmup, stream, warm_s)
     record("all_gather_bf16", P * M * 2 + P * P * M * 2, ms, "all_gather, P=8 x 16,777,216 bf16")
+    # the same all-gather with the ranks in staggered slabs, as in the headline
+    sx, _ = rank_slab(P, M * 2, dev)
+    for d, t in zip(sx, dx):
+        d.copy_(t)
     del dx, dy
+    sy, _ = rank_slab(P, P * M * 2, dev)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_gather(sx, sy, P, M, ccl.CCL_BFLOAT16, stream)),
+               steps, warmup, stream, warm_s)
+    record("all_gather_bf16_slab_placement", P * M * 2 + P * P * M * 2, ms,
+           "all_gather, P=8 x 16,777,216 bf16, ranks in staggered slabs as in the headline")
+    del sx, sy
     torch.cuda.empty_cache()
 
     # the headline all-reduce with the caching allocator's placement (one
