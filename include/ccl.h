@@ -25,6 +25,13 @@
  *     was touched.  CCL_ERR_HIP reports a failed launch; faults inside a
  *     kernel surface at the caller's next synchronization.
  *   - A count of 0 is a valid no-op (pointers are then not inspected).
+ *   - Host threads: any call may run concurrently with others from other
+ *     threads, on the same or different streams.  Calls in flight together
+ *     must not write a buffer another of them reads or writes; the stream
+ *     order is the caller's to arrange.  A plan may be shared by concurrent
+ *     calls (its device table is built once per device and chunk size under
+ *     a lock); destroying it while another call still uses it is an error the
+ *     library does not detect.
  *   - Reductions are computed per element as a fold in rank order 0..P-1 that
  *     starts from rank 0's value and accumulates in fp32 (bf16 and fp16
  *     inputs are widened exactly, the fp32 result is rounded back once, to
