@@ -175,10 +175,11 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
       Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
       if (overlap(x, y) && y.lo != x.lo + (uint64_t)s * out_bytes) return CCL_ERR_ALIASING;
     }
-  // Past ~160 MiB per rank (at 7 <= P <= 12) the LDS pipeline overtakes the
+  // Past ~160 MiB per rank (at P = 7, 8) the LDS pipeline overtakes the
   // register-direct kernel (at P = 8: 6.3 vs 6.0 TB/s at 192-256 MiB, while
-  // at 32-128 MiB the register-direct kernel leads by 6-9 %).
-  if (nranks >= 7 && nranks <= 12 && in_bytes > (160ull << 20)) {
+  // at 32-128 MiB the register-direct kernel leads by 6-9 %).  From P = 9 on
+  // the register-direct kernel with its own defaults leads at every size.
+  if (nranks >= 7 && nranks <= 8 && in_bytes > (160ull << 20)) {
     if (!l.stages_set) l.stages = 2;
     if (!l.occupancy_set) l.occupancy = 2;
   }
@@ -276,7 +277,7 @@ ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t 
     if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
   }
   // the reduce-scatter kernels' size rule (see ccl_reduce_scatter)
-  if (nranks >= 7 && nranks <= 12 && bytes > (160ull << 20)) {
+  if (nranks >= 7 && nranks <= 8 && bytes > (160ull << 20)) {
     if (!l.stages_set) l.stages = 2;
     if (!l.occupancy_set) l.occupancy = 2;
   }

@@ -38,12 +38,14 @@ inline OpDefaults default_launch(Op op, int P) {
       return {4096, 1, 1, 3};
     case OP_RS:
       if (P <= 2) return {8192, 1, 2, 4};
+      if (P >= 9 && P <= 12) return {4096, 1, 1, 4};
       return {8192, 1, 2, 3};
     case OP_AG:
       if (P <= 2) return {8192, 1, 2, 4};
-      if (P >= 7 && P <= 12) return {4096, 2, 2, 3};
-      if (P >= 13) return {8192, 1, 2, 1};
-      return {8192, 1, 2, 3};
+      if (P <= 4) return {8192, 1, 2, 3};
+      if (P <= 6) return {4096, 1, 1, 4};
+      if (P <= 8) return {4096, 2, 2, 3};
+      return {4096, 1, 1, 3};
     case OP_RMSNORM:
       return {16384, 1, 1, 0};
     case OP_RESHARD_FP8:

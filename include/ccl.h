@@ -80,13 +80,17 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU;
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
- *                   <= 4 (P <= 2) or 3 WGs per CU; for 7 <= P <= 12 with more
+ *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
+ *                   <= 4 WGs per CU for 9 <= P <= 12; for P = 7, 8 with more
  *                   than 160 MiB per rank, the 2-stage LDS pipeline with <= 2
  *                   WGs per CU
  *   broadcast       as all-gather
- *   all-gather      7 <= P <= 12: LDS pipeline, 2 stages, 4 KiB chunks,
- *                   <= 3 WGs per CU; otherwise register-direct, 8 KiB chunks,
- *                   unroll 2, <= 4 (P <= 2), 3, or 1 (P >= 13) WGs per CU
+ *   all-gather      P <= 4: register-direct, 8 KiB chunks, unroll 2, <= 4
+ *                   (P <= 2) or 3 WGs per CU; P = 5, 6: register-direct,
+ *                   4 KiB chunks, unroll 1, <= 4 WGs per CU; P = 7, 8: LDS
+ *                   pipeline, 2 stages, 4 KiB chunks, <= 3 WGs per CU;
+ *                   P >= 9: register-direct, 4 KiB chunks, unroll 1, <= 3
+ *                   WGs per CU
  *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
  *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
  *                   two or more: 32 KiB chunks, <= 2 WGs per CU,

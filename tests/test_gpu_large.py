@@ -145,9 +145,10 @@ def test_all_reduce_rmsnorm_past_4gib_per_rank():
 
 @pytest.mark.parametrize("P", [7, 8, 12])
 def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
-    """At 7 <= P <= 12 reduce-scatter and reduce switch from the register-direct
-    kernel to the LDS pipeline past 160 MiB per rank; both sides of that
-    switch must give the oracle's values (sum, sampled)."""
+    """At P = 7, 8 reduce-scatter and reduce switch from the register-direct
+    kernel to the LDS pipeline past 160 MiB per rank (P = 12 stays
+    register-direct with its own defaults); both sides of that size must give
+    the oracle's values (sum, sampled)."""
     TORCH = {"bf16": torch.int16, "f32": torch.int32}
     for dtype, per_rank_mib in (("bf16", 144), ("bf16", 176), ("f32", 168)):
         esz = 2 if dtype == "bf16" else 4
