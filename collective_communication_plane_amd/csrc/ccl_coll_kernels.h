@@ -285,16 +285,46 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
 
     for (uint64_t v = v0 + threadIdx.x; v < v1; v += kThreads) {
       u32x4 x[NI];
+      if constexpr (KIND == KIND_RS) {
+        // Reduce-scatter (P inputs, one output): every rank's two blocks are
+        // requested before the first one is realigned, so the P round trips
+        // overlap.  Without a shift the second block repeats the first (the
+        // block after it may lie outside the input).  The nontemporal choice
+        // is made once around compile-time loads, since a load picked at run
+        // time is merged into a plain one.
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        u32x4 A[NI], B[NI];
+        if (ntl) {
 #pragma unroll
-      for (int r = 0; r < NI; ++r) {
-        if (r < ni) {
-          const char *p = ib[r] + v * kVecBytes;
-          const u32x4 A = ntl ? ld_nt(p) : ld_plain(p);
-          if (sh[r]) {
-            const u32x4 B = ntl ? ld_nt(p + kVecBytes) : ld_plain(p + kVecBytes);
-            x[r] = realign16(A, B, sh[r]);
-          } else {
-            x[r] = A;
+          for (int r = 0; r < NI; ++r) {
+            A[r] = r < ni ? ld<true>(ib[r] + v * kVecBytes) : zero;
+            B[r] = r < ni ? ld<true>(ib[r] + v * kVecBytes + (sh[r] ? kVecBytes : 0)) : zero;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < NI; ++r) {
+            A[r] = r < ni ? ld<false>(ib[r] + v * kVecBytes) : zero;
+            B[r] = r < ni ? ld<false>(ib[r] + v * kVecBytes + (sh[r] ? kVecBytes : 0)) : zero;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < NI; ++r) x[r] = r < ni ? realign16(A[r], B[r], sh[r]) : zero;
+      } else {
+        // All-reduce and all-gather: rank by rank, the second block only
+        // where there is a shift, through cacheable loads.  With P outputs
+        // as well, this measured faster than every load in flight at once,
+        // and nontemporal loads gave no gain here.
+#pragma unroll
+        for (int r = 0; r < NI; ++r) {
+          if (r < ni) {
+            const char *p = ib[r] + v * kVecBytes;
+            const u32x4 A = ld_plain(p);
+            if (sh[r]) {
+              const u32x4 B = ld_plain(p + kVecBytes);
+              x[r] = realign16(A, B, sh[r]);
+            } else {
+              x[r] = A;
+            }
           }
         }
       }

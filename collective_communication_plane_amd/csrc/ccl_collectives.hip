@@ -103,12 +103,16 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // The realigning kernel reads two blocks per input vector and wants other
   // chunks and residency than the aligned kernels whose defaults it would
   // otherwise inherit (reduce-scatter at P = 3 and 12: 2800-3200 GB/s under
-  // those, 4800-5800 with these).
+  // those, 4800-5800 with these).  Its loads stay cacheable: a lane's second
+  // block is its neighbour's first, which a nontemporal load does not keep
+  // for it (the ragged reduce-scatter ran 4-15 % slower with them).
   uint64_t chunk_bytes = l.chunk_bytes;
   int occupancy = l.occupancy;
   if (realign) {
-    if (!l.chunk_set) chunk_bytes = 4096;
-    if (!l.occupancy_set) occupancy = d.kind != KIND_AG ? 8 : d.P <= 6 ? 4 : 3;
+    const bool many = d.kind == KIND_RS && d.P > 8;
+    if (!l.chunk_set) chunk_bytes = many ? 8192 : 4096;
+    if (!l.occupancy_set) occupancy = d.kind != KIND_AG ? (many ? 4 : 8) : d.P <= 6 ? 4 : 3;
+    if (!l.nt_set && d.kind == KIND_RS) a.flags &= ~1;
   }
   p.occupancy = occupancy;
   a.chunk_vecs = chunk_bytes / kVecBytes;

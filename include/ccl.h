@@ -103,8 +103,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   nontemporal and occupancy and ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
  * use a register-direct kernel that realigns the inputs in VGPRs; unless the
- * caller sets them, it runs 4 KiB chunks with <= 8 WGs per CU (all-gather:
- * <= 4 for P <= 6, <= 3 above).
+ * caller sets them, it runs 4 KiB chunks with <= 8 WGs per CU (reduce-scatter
+ * above P = 8: 8 KiB chunks, <= 4 WGs per CU; all-gather: <= 4 for P <= 6,
+ * <= 3 above) and cacheable loads (nontemporal stores only; its all-reduce
+ * and all-gather forms always load through the cache).
  * A zero field means "the default for this call"; out-of-range values give
  * CCL_ERR_INVALID_ARG.  None of these fields changes any result.
  *
