@@ -350,6 +350,15 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
                steps, warmup, stream, warm_s)
     record("all_reduce_rmsnorm_bf16", 2 * P * rows * hidden * 2 + hidden * 2, ms,
            "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16")
+    # the same bytes in 32 KiB rows, which take the row-pipelined kernel
+    rows, hidden = 8192, 16384
+    gamma = torch.from_numpy(si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
+                             .view(np.int16).copy()).to(dev)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, gamma, 1e-6,
+                                                            ccl.CCL_BFLOAT16, stream)),
+               steps, warmup, stream, warm_s)
+    record("all_reduce_rmsnorm_bf16_long_rows", 2 * P * rows * hidden * 2 + hidden * 2, ms,
+           "all_reduce sum + RMSNorm per row, P=8 x 8192 x 16384 bf16 (row-pipelined)")
     del dx, dy
     torch.cuda.empty_cache()
 

@@ -101,6 +101,12 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
   }
   if ((op == OP_RESHARD || op == OP_RESHARD_FP8) && explicit_stages && l.stages != 1)
     return CCL_ERR_UNSUPPORTED;
+  // the fused RMSNorm: 1 = one row at a time, 2 = two rows software-pipelined
+  if (op == OP_RMSNORM) {
+    if (l.stages > 2) return CCL_ERR_UNSUPPORTED;
+    *out = l;
+    return CCL_OK;
+  }
   if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) {
     if (explicit_stages) return CCL_ERR_INVALID_ARG;
     l.stages = 1;
@@ -245,11 +251,15 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
       if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
     }
   }
-  // Default residency by row length: rows of 4-8 KiB per rank run best with at
-  // most 3 workgroups per CU, shorter and longer ones uncapped.
+  // Defaults by row length.  Rows longer than 16 KiB per rank: the
+  // row-pipelined kernel with one workgroup per CU (+2.5-4.6 % at 24-32 KiB);
+  // up to 16 KiB: one workgroup per row, at most 3 per CU for rows of 4-8 KiB,
+  // shorter and longer ones uncapped.
+  const uint64_t row_bytes = hidden * sz;
+  if (!l.stages_set) l.stages = row_bytes > 16384 ? 2 : 1;
   if (!l.occupancy_set) {
-    const uint64_t row_bytes = hidden * sz;
-    l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+    if (l.stages == 2) l.occupancy = 1;
+    else l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
   }
   ccl::RmsDesc d{nranks, dtype, rows, hidden, eps, send, recv, gamma};
   return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream);

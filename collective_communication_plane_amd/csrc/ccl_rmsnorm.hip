@@ -133,8 +133,117 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
   }
 }
 
+// The row's inverse RMS from each lane's partial sum of squares: a wave
+// butterfly, then the four waves in order through `part` (one slot per wave).
+// One block-wide barrier; the caller alternates between two `part` arrays so
+// that a wave cannot overwrite a slot another wave has yet to read.
+__device__ __forceinline__ float row_inv_rms(float ss, float *part, uint32_t hidden, float eps) {
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) total += part[w];
+  return 1.0f / sqrtf(total / (float)hidden + eps);
+}
+
+// The same computation as ar_rmsnorm_kernel, software-pipelined over a
+// workgroup's rows so that reads and writes interleave.  The grid is
+// persistent (workgroup w takes rows w, w + G, w + 2G, ...).  While the
+// normalised row k is stored, 16-byte vector by 16-byte vector, the inputs of
+// the workgroup's next row are loaded and folded into a second LDS row
+// buffer: each lane keeps one vector per rank in flight for the next row and
+// one per output for the current one, so HBM sees the all-reduce's mix of
+// reads and writes instead of a whole row of reads followed by a whole row of
+// writes.  Each lane only touches the row-buffer vectors it owns, so the one
+// barrier per row (the norm's) is all the synchronisation there is; the sum
+// of squares runs in the same order as ar_rmsnorm_kernel's, so both give
+// identical bits.  Row k is read completely before any of it is stored, so
+// the call may still run in place.
+template <int DT, int PMAX, bool NTL, bool NTS>
+__global__ void __launch_bounds__(kThreads) ar_rmsnorm_pipe_kernel(RmsArgs a) {
+  constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
+  constexpr int V = kVecBytes / esz;
+  extern __shared__ u32x4 row_bufs[];  // two rows of row_vecs vectors
+  __shared__ float wave_part[2][kThreads / 64];
+  const int P = a.P;
+  const uint64_t row_bytes = (uint64_t)a.hidden * esz;
+  uint64_t row = blockIdx.x;
+  if (row >= a.rows) return;
+  u32x4 *cur = row_bufs, *nxt = row_bufs + a.row_vecs;
+
+  // prologue: fold the first row
+  float ss = 0.f;
+#pragma unroll 1
+  for (uint32_t v = threadIdx.x; v < a.row_vecs; v += kThreads) {
+    u32x4 x[PMAX];
+#pragma unroll
+    for (int r = 0; r < PMAX; ++r)
+      x[r] = r < P ? ld<NTL>(a.in[r] + row * row_bytes + (uint64_t)v * kVecBytes)
+                   : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
+    cur[v] = sv;
+    float f[8];
+    widen_vec<DT>(sv, f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) ss += f[e] * f[e];
+  }
+  int par = 0;
+  float inv = row_inv_rms(ss, wave_part[par], a.hidden, a.eps);
+
+  for (;;) {
+    const uint64_t next = row + gridDim.x;
+    const bool more = next < a.rows;
+    const uint64_t base = row * row_bytes, nbase = next * row_bytes;
+    ss = 0.f;
+#pragma unroll 1
+    for (uint32_t v = threadIdx.x; v < a.row_vecs; v += kThreads) {
+      const uint64_t off = (uint64_t)v * kVecBytes;
+      // gamma first: vector loads complete in issue order, so the stores
+      // below then wait only for gamma, not for the next row's inputs
+      const u32x4 gv = ld_plain(a.gamma + off);
+      u32x4 x[PMAX];
+      if (more) {
+#pragma unroll
+        for (int r = 0; r < PMAX; ++r)
+          x[r] = r < P ? ld<NTL>(a.in[r] + nbase + off) : u32x4{0u, 0u, 0u, 0u};
+      }
+      float g[8], f[8], y[8];
+      widen_vec<DT>(gv, g);
+      widen_vec<DT>(cur[v], f);
+#pragma unroll
+      for (int e = 0; e < V; ++e) y[e] = (f[e] * inv) * g[e];
+      const u32x4 o = narrow_vec<DT>(y);
+#pragma unroll
+      for (int q = 0; q < PMAX; ++q)
+        if (q < P) st<NTS>(a.out[q] + base + off, o);
+      if (more) {
+        const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
+        nxt[v] = sv;
+        float h[8];
+        widen_vec<DT>(sv, h);
+#pragma unroll
+        for (int e = 0; e < V; ++e) ss += h[e] * h[e];
+      }
+    }
+    if (!more) break;
+    par ^= 1;
+    inv = row_inv_rms(ss, wave_part[par], a.hidden, a.eps);
+    u32x4 *t = cur;
+    cur = nxt;
+    nxt = t;
+    row = next;
+  }
+}
+
 template <int DT, bool NTL, bool NTS>
-hipError_t launch_p(const RmsArgs &a, unsigned grid, size_t lds, hipStream_t st) {
+hipError_t launch_p(const RmsArgs &a, bool pipe, unsigned grid, size_t lds, hipStream_t st) {
+  if (pipe) {
+    if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+    else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 8, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+    else hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 16, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+    return hipGetLastError();
+  }
   if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
   else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
   else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
@@ -142,11 +251,12 @@ hipError_t launch_p(const RmsArgs &a, unsigned grid, size_t lds, hipStream_t st)
 }
 
 template <int DT>
-hipError_t launch_nt(const RmsArgs &a, const Launch &l, unsigned grid, size_t lds, hipStream_t st) {
-  if (l.nt_load && l.nt_store) return launch_p<DT, true, true>(a, grid, lds, st);
-  if (l.nt_load) return launch_p<DT, true, false>(a, grid, lds, st);
-  if (l.nt_store) return launch_p<DT, false, true>(a, grid, lds, st);
-  return launch_p<DT, false, false>(a, grid, lds, st);
+hipError_t launch_nt(const RmsArgs &a, const Launch &l, bool pipe, unsigned grid, size_t lds,
+                     hipStream_t st) {
+  if (l.nt_load && l.nt_store) return launch_p<DT, true, true>(a, pipe, grid, lds, st);
+  if (l.nt_load) return launch_p<DT, true, false>(a, pipe, grid, lds, st);
+  if (l.nt_store) return launch_p<DT, false, true>(a, pipe, grid, lds, st);
+  return launch_p<DT, false, false>(a, pipe, grid, lds, st);
 }
 
 }  // namespace
@@ -164,16 +274,29 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   a.row_vecs = (uint32_t)(d.hidden * esz / kVecBytes);
   a.eps = d.eps;
   a.P = d.P;
-  uint64_t grid = l.workgroups ? (uint64_t)l.workgroups : d.rows;
+  // stages = 2: the row-pipelined kernel on a persistent grid of (residency
+  // cap, else 1) workgroups per CU; stages = 1: one workgroup per row.
+  const bool pipe = l.stages == 2;
+  uint64_t grid = d.rows;
+  if (l.workgroups) {
+    grid = (uint64_t)l.workgroups;
+  } else if (pipe) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
+    const int cus = device_cu_count(dev);
+    if (cus <= 0) return CCL_ERR_HIP;
+    grid = (uint64_t)cus * (uint64_t)(l.occupancy > 0 ? l.occupancy : 1);
+  }
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, d.rows), 1u << 30);
-  // the row buffer, or more when the launch caps residency through LDS
-  const size_t row_lds = (size_t)a.row_vecs * kVecBytes;
-  const size_t lds = std::max(row_lds, occupancy_lds(l.occupancy, (kThreads / 64) * sizeof(float)));
+  // the row buffer(s), or more when the launch caps residency through LDS
+  const size_t row_lds = (size_t)a.row_vecs * kVecBytes * (pipe ? 2 : 1);
+  const size_t static_lds = (kThreads / 64) * sizeof(float) * (pipe ? 2 : 1);
+  const size_t lds = std::max(row_lds, occupancy_lds(l.occupancy, static_lds));
   hipError_t err;
   switch (d.dtype) {
-    case CCL_FLOAT32: err = launch_nt<CCL_FLOAT32>(a, l, (unsigned)grid, lds, stream); break;
-    case CCL_BFLOAT16: err = launch_nt<CCL_BFLOAT16>(a, l, (unsigned)grid, lds, stream); break;
-    default: err = launch_nt<CCL_FLOAT16>(a, l, (unsigned)grid, lds, stream); break;
+    case CCL_FLOAT32: err = launch_nt<CCL_FLOAT32>(a, l, pipe, (unsigned)grid, lds, stream); break;
+    case CCL_BFLOAT16: err = launch_nt<CCL_BFLOAT16>(a, l, pipe, (unsigned)grid, lds, stream); break;
+    default: err = launch_nt<CCL_FLOAT16>(a, l, pipe, (unsigned)grid, lds, stream); break;
   }
   return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }

@@ -97,10 +97,14 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   nontemporal stores only
  *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
- *   all-reduce + RMSNorm  one workgroup per row; <= 3 WGs per CU for rows of
- *                   4-8 KiB, otherwise residency bounded only by registers and
- *                   the row buffer it keeps in LDS; it reads workgroups,
- *                   nontemporal and occupancy and ignores the rest
+ *   all-reduce + RMSNorm  rows of up to 16 KiB per rank: one workgroup per
+ *                   row; <= 3 WGs per CU for rows of 4-8 KiB, otherwise
+ *                   residency bounded only by registers and the row buffer it
+ *                   keeps in LDS.  Longer rows: the row-pipelined kernel
+ *                   (stages = 2) on a persistent grid of one workgroup per CU.
+ *                   It reads workgroups, stages (1 or 2; 3 and 4 give
+ *                   CCL_ERR_UNSUPPORTED), nontemporal and occupancy and
+ *                   ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
  * use a register-direct kernel that realigns the inputs in VGPRs; unless the
  * caller sets them, it runs 4 KiB chunks with <= 8 WGs per CU (reduce-scatter
@@ -123,6 +127,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                `stages` LDS buffers with asynchronous global->LDS loads,
  *                consumer waves fold and store them (clamped so the ring
  *                fits in 128 KiB).  The reshard copy is register-direct only.
+ *                For the fused RMSNorm: 1 = one row at a time per workgroup,
+ *                2 = two rows software-pipelined (the next row's inputs are
+ *                loaded and folded while the current row is stored).
  *   unroll       register-direct only: 16-byte vectors each lane keeps in
  *                flight per rank (1, 2 or 4; 4 is used as 2 when P > 8); for
  *                the fp8 reshard, vectors each lane loads before quantizing.

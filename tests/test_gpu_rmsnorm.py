@@ -43,35 +43,44 @@ def run(xs, rows, hidden, gamma, eps, dtype, in_place=False, cfg=None):
     return [b.download(NP[dtype]) for b in dy]
 
 
+@pytest.mark.parametrize("stages", [1, 2])
 @pytest.mark.parametrize("P", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("hidden", [64, 1024, 7168, 8192])
-def test_matches_oracle(P, dtype, hidden):
+def test_matches_oracle(P, dtype, hidden, stages):
     if dtype == "f32" and hidden > 8192:
         pytest.skip("fp32 rows are limited to 8192 elements")
     rows, eps = 19, 1e-6
     xs = si.rank_buffers(P, rows * hidden, dtype, "normal", seed=P + hidden)
     gamma = si.rank_buffers(1, hidden, dtype, "uniform", seed=7)[0]
-    got = run(xs, rows, hidden, gamma, eps, dtype)
+    # stages=2 on a grid of 5 workgroups: every workgroup pipelines 3-4 rows
+    cfg = ccl.LaunchConfig(stages=2, workgroups=5) if stages == 2 else ccl.LaunchConfig(stages=1)
+    got = run(xs, rows, hidden, gamma, eps, dtype, cfg=cfg)
     want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, eps, dtype)
     for q in range(P):
         assert_rmsnorm_parity(got[q], want[q], dtype, hidden, f"P={P} {dtype} H={hidden}")
         np.testing.assert_array_equal(got[q], got[0])
 
 
-def test_bf16_hidden_16384_and_in_place():
+@pytest.mark.parametrize("cfg", [None, dict(stages=1), dict(stages=2, workgroups=2)])
+def test_bf16_hidden_16384_and_in_place(cfg):
     P, rows, hidden = 4, 9, 16384
     xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=3)
     gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=4)[0]
     want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, 1e-5, "bf16")
-    got = run(xs, rows, hidden, gamma, 1e-5, "bf16", in_place=True)
+    got = run(xs, rows, hidden, gamma, 1e-5, "bf16", in_place=True,
+              cfg=ccl.LaunchConfig(**cfg) if cfg else None)
     for q in range(P):
         assert_rmsnorm_parity(got[q], want[q], "bf16", hidden, "in place")
 
 
 @pytest.mark.parametrize("cfg", [dict(workgroups=1), dict(workgroups=7), dict(occupancy=1),
                                  dict(occupancy=32), dict(nontemporal=1), dict(nontemporal=2),
-                                 dict(nontemporal=4)])
+                                 dict(nontemporal=4), dict(stages=1), dict(stages=2),
+                                 dict(stages=2, workgroups=1), dict(stages=2, workgroups=39),
+                                 dict(stages=2, workgroups=40), dict(stages=2, workgroups=41),
+                                 dict(stages=2, occupancy=1), dict(stages=2, occupancy=3),
+                                 dict(stages=2, nontemporal=4)])
 def test_launch_config_does_not_change_results(cfg):
     P, rows, hidden = 8, 40, 4096
     xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=9)
@@ -98,6 +107,8 @@ def test_rejections():
                                       st) == ccl.CCL_ERR_INVALID_ARG
     assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, hidden, g.ptr, 1e-6, ccl.CCL_INT32,
                                       st) == ccl.CCL_ERR_INVALID_ARG
+    assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, hidden, g.ptr, 1e-6, ccl.CCL_BFLOAT16,
+                                      st, ccl.LaunchConfig(stages=3)) == ccl.CCL_ERR_UNSUPPORTED
     assert ccl.ccl_all_reduce_rmsnorm(send, [recv[0], recv[0] + 16], P, rows, hidden, g.ptr, 1e-6,
                                       ccl.CCL_BFLOAT16, st) == ccl.CCL_ERR_ALIASING
     torch.cuda.synchronize()
@@ -105,16 +116,19 @@ def test_rejections():
         assert (b.base == b.fill).all().item()
 
 
-def test_full_size_sampled_rows():
+@pytest.mark.parametrize("stages", [1, 2])
+def test_full_size_sampled_rows(stages):
     """P=8, 16384 tokens x 8192 hidden bf16 (256 MiB per rank): exact replica
-    identity on the GPU and sampled rows against the oracle."""
+    identity on the GPU and sampled rows against the oracle, one workgroup per
+    row and row-pipelined."""
     P, rows, hidden = 8, 16384, 8192
     dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=DEV)
     gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
     dg = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
     dy = [torch.empty_like(t) for t in dx]
     ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16,
-                                         torch.cuda.current_stream()))
+                                         torch.cuda.current_stream(),
+                                         ccl.LaunchConfig(stages=stages)))
     torch.cuda.synchronize()
     for q in range(1, P):
         assert torch.equal(dy[q].view(torch.int16), dy[0].view(torch.int16))
