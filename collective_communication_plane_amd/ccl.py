@@ -51,7 +51,7 @@ class LaunchConfig(ctypes.Structure):
     _fields_ = [("chunk_bytes", ctypes.c_uint64), ("workgroups", ctypes.c_int32),
                 ("stages", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("nontemporal", ctypes.c_int32), ("occupancy", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("store_policy", ctypes.c_int32)]
 
 
 class Placement(ctypes.Structure):

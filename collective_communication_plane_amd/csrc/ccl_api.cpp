@@ -93,7 +93,12 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
       l.nt_store = (cfg->nontemporal >> 1) & 1;
       l.nt_set = true;
     }
-    if (cfg->occupancy < 0 || cfg->occupancy > 32 || cfg->reserved != 0) return CCL_ERR_INVALID_ARG;
+    if (cfg->occupancy < 0 || cfg->occupancy > 32) return CCL_ERR_INVALID_ARG;
+    if (cfg->store_policy < 0 || cfg->store_policy > 2) return CCL_ERR_INVALID_ARG;
+    if (cfg->store_policy) {
+      l.store_wt = cfg->store_policy == 1;
+      l.store_pol_set = true;
+    }
     if (cfg->occupancy) {
       l.occupancy = cfg->occupancy;
       l.occupancy_set = true;

@@ -45,7 +45,9 @@ struct CollArgs {
   uint64_t chunks_per_seg;
   uint64_t total_chunks;
   int P;
-  int flags;                      // bit 0: nontemporal loads, bit 1: nontemporal stores
+  // bit 0: nontemporal loads, bit 1: nontemporal stores, bit 2: those stores
+  // write-through (st_wt; the host sets it only for chunks below 2 GiB)
+  int flags;
 };
 
 // Which kernel family a launch uses, with its resolved launch shape.
@@ -154,7 +156,7 @@ __global__ void __launch_bounds__(kThreads)
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
 
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int s = (int)(c / a.chunks_per_seg);
@@ -207,7 +209,11 @@ __global__ void __launch_bounds__(kThreads)
           u32x4 y;
           if constexpr (KIND == KIND_AG) y = x[u][0];
           else y = fold_vec<DT, OP, NI>(x[u], ni);
-          if (nts) {
+          if (wts) {
+#pragma unroll
+            for (int q = 0; q < NO; ++q)
+              if (q < no) st_wt(ob[q] + v0 * kVecBytes, (vv - v0) * kVecBytes, y);
+          } else if (nts) {
 #pragma unroll
             for (int q = 0; q < NO; ++q)
               if (q < no) st_nt(ob[q] + vv * kVecBytes, y);
@@ -256,7 +262,7 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
 
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int s = (int)(c / a.chunks_per_seg);
@@ -331,7 +337,11 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
       u32x4 y;
       if constexpr (KIND == KIND_AG) y = x[0];
       else y = fold_vec<DT, OP, NI>(x, ni);
-      if (nts) {
+      if (wts) {
+#pragma unroll
+        for (int q = 0; q < NO; ++q)
+          if (q < no) st_wt(ob[q] + v0 * kVecBytes, (v - v0) * kVecBytes, y);
+      } else if (nts) {
 #pragma unroll
         for (int q = 0; q < NO; ++q)
           if (q < no) st_nt(ob[q] + v * kVecBytes, y);
@@ -461,7 +471,7 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
@@ -552,9 +562,10 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
 #pragma unroll
         for (int q = 0; q < NO; ++q)
           if (q < no) {
-            char *d = out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes;
-            if (nts) st_nt(d, y);
-            else st_plain(d, y);
+            char *d = out_at<KIND>(a, s, q, head, esz);
+            if (wts) st_wt(d + k.v0 * kVecBytes, (vv - k.v0) * kVecBytes, y);
+            else if (nts) st_nt(d + vv * kVecBytes, y);
+            else st_plain(d + vv * kVecBytes, y);
           }
       }
       cursor_next(a, k);

@@ -34,6 +34,41 @@ __device__ __forceinline__ void st(char *p, u32x4 v) {
   else st_plain(p, v);
 }
 
+// Write-through streaming store: a buffer store with the nontemporal and
+// device-scope (sc1) cache-policy bits.  At device scope the L2 of the issuing
+// XCD passes the line on to memory instead of holding it dirty, which on
+// MI355X streams 2-4 % more bytes per second through an all-reduce and up to
+// 8 % through an all-gather at the same launch shape (it needs >= 4 resident
+// workgroups per CU to cover its longer completion time).  The buffer
+// resource is built from `base`, which the callers keep uniform across the
+// workgroup (a per-lane base would make the compiler loop over lanes); the
+// lane's byte offset from it is below 2^31.
+__device__ __forceinline__ void st_wt(char *base, uint64_t off, u32x4 v) {
+  constexpr int kPolNtSc1 = 2 | 16;  // nt | sc1
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolNtSc1);
+}
+
+// A pointer the caller knows to be the same in every lane, moved to scalar
+// registers so that a buffer resource can be built from it without a loop
+// over lanes.
+__device__ __forceinline__ char *wave_uniform(char *p) {
+  const uint64_t u = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (char *)(((uint64_t)hi << 32) | lo);
+}
+
+// Store policy of the kernels that take it as a template argument.
+enum StorePol { ST_PLAIN = 0, ST_NT = 1, ST_WT = 2 };
+template <int POL>
+__device__ __forceinline__ void st_pol(char *base, uint64_t off, u32x4 v) {
+  if constexpr (POL == ST_WT) st_wt(base, off, v);
+  else if constexpr (POL == ST_NT) st_nt(base + off, v);
+  else st_plain(base + off, v);
+}
+
 // bf16 -> fp32 is exact: the bf16 pattern is the upper half of the fp32 one.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -43,8 +43,7 @@ inline OpDefaults default_launch(Op op, int P) {
     case OP_AG:
       if (P <= 2) return {8192, 1, 2, 4};
       if (P <= 4) return {8192, 1, 2, 3};
-      if (P <= 6) return {4096, 1, 1, 4};
-      if (P <= 8) return {4096, 2, 2, 3};
+      if (P <= 8) return {4096, 1, 1, 4};
       return {4096, 1, 1, 3};
     case OP_RMSNORM:
       return {16384, 1, 1, 0};
@@ -80,6 +79,8 @@ struct Launch {
   bool stages_set = false;     // stages came from the caller
   bool occupancy_set = false;  // occupancy came from the caller
   bool nt_set = false;         // nontemporal hints came from the caller
+  bool store_wt = true;        // nontemporal stores write through (st_wt)
+  bool store_pol_set = false;  // store_wt came from the caller
 };
 
 // Dynamic LDS to request so that at most `occupancy` workgroups fit on a CU

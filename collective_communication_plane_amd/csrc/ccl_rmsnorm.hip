@@ -81,8 +81,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 // the only synchronisation.  A lane keeps one vector per rank in flight:
 // holding several (in registers) measured slower, since more concurrent
 // streams only add DRAM page conflicts.
-// NTL / NTS: nontemporal loads / stores (template arguments, see ld / st).
-template <int DT, int PMAX, bool NTL, bool NTS>
+// NTL: nontemporal loads (template argument, see ld); SP: store policy
+// (StorePol: plain, nontemporal, or write-through from the row's base).
+template <int DT, int PMAX, bool NTL, int SP>
 __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int V = kVecBytes / esz;
@@ -125,10 +126,7 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_kernel(RmsArgs a) {
       const u32x4 o = narrow_vec<DT>(y);
 #pragma unroll
       for (int q = 0; q < PMAX; ++q)
-        if (q < P) {
-          char *d = a.out[q] + base + (uint64_t)v * kVecBytes;
-          st<NTS>(d, o);
-        }
+        if (q < P) st_pol<SP>(a.out[q] + base, (uint64_t)v * kVecBytes, o);
     }
   }
 }
@@ -160,7 +158,7 @@ __device__ __forceinline__ float row_inv_rms(float ss, float *part, uint32_t hid
 // of squares runs in the same order as ar_rmsnorm_kernel's, so both give
 // identical bits.  Row k is read completely before any of it is stored, so
 // the call may still run in place.
-template <int DT, int PMAX, bool NTL, bool NTS>
+template <int DT, int PMAX, bool NTL, int SP>
 __global__ void __launch_bounds__(kThreads) ar_rmsnorm_pipe_kernel(RmsArgs a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int V = kVecBytes / esz;
@@ -216,7 +214,7 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_pipe_kernel(RmsArgs a) {
       const u32x4 o = narrow_vec<DT>(y);
 #pragma unroll
       for (int q = 0; q < PMAX; ++q)
-        if (q < P) st<NTS>(a.out[q] + base + off, o);
+        if (q < P) st_pol<SP>(a.out[q] + base, off, o);
       if (more) {
         const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, P);
         nxt[v] = sv;
@@ -236,27 +234,40 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_pipe_kernel(RmsArgs a) {
   }
 }
 
-template <int DT, bool NTL, bool NTS>
+template <int DT, bool NTL, int SP>
 hipError_t launch_p(const RmsArgs &a, bool pipe, unsigned grid, size_t lds, hipStream_t st) {
   if (pipe) {
-    if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-    else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 8, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-    else hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 16, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+    if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 4, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+    else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 8, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+    else hipLaunchKernelGGL((ar_rmsnorm_pipe_kernel<DT, 16, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
     return hipGetLastError();
   }
-  if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-  else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-  else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  if (a.P <= 4) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 4, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (a.P <= 8) hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 8, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((ar_rmsnorm_kernel<DT, 16, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t launch_nt(const RmsArgs &a, const Launch &l, bool pipe, unsigned grid, size_t lds,
                      hipStream_t st) {
-  if (l.nt_load && l.nt_store) return launch_p<DT, true, true>(a, pipe, grid, lds, st);
-  if (l.nt_load) return launch_p<DT, true, false>(a, pipe, grid, lds, st);
-  if (l.nt_store) return launch_p<DT, false, true>(a, pipe, grid, lds, st);
-  return launch_p<DT, false, false>(a, pipe, grid, lds, st);
+  // Write-through stores by default only for the row-pipelined kernel on rows
+  // that start on 256-byte boundaries (+4 % there; -0.6 % for one row per
+  // workgroup at 16 KiB rows).
+  bool wt = l.store_wt;
+  if (!l.store_pol_set) {
+    wt = pipe && (a.row_vecs * kVecBytes) % 256 == 0;
+    for (int q = 0; q < a.P; ++q) wt = wt && (uintptr_t)a.out[q] % 256 == 0;
+  }
+  const int sp = !l.nt_store ? ST_PLAIN : wt ? ST_WT : ST_NT;
+  if (l.nt_load) {
+    if (sp == ST_WT) return launch_p<DT, true, ST_WT>(a, pipe, grid, lds, st);
+    if (sp == ST_NT) return launch_p<DT, true, ST_NT>(a, pipe, grid, lds, st);
+    return launch_p<DT, true, ST_PLAIN>(a, pipe, grid, lds, st);
+  }
+  if (sp == ST_WT) return launch_p<DT, false, ST_WT>(a, pipe, grid, lds, st);
+  if (sp == ST_NT) return launch_p<DT, false, ST_NT>(a, pipe, grid, lds, st);
+  return launch_p<DT, false, ST_PLAIN>(a, pipe, grid, lds, st);
 }
 
 }  // namespace

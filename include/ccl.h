@@ -86,11 +86,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   WGs per CU
  *   broadcast       as all-gather
  *   all-gather      P <= 4: register-direct, 8 KiB chunks, unroll 2, <= 4
- *                   (P <= 2) or 3 WGs per CU; P = 5, 6: register-direct,
- *                   4 KiB chunks, unroll 1, <= 4 WGs per CU; P = 7, 8: LDS
- *                   pipeline, 2 stages, 4 KiB chunks, <= 3 WGs per CU;
- *                   P >= 9: register-direct, 4 KiB chunks, unroll 1, <= 3
- *                   WGs per CU
+ *                   (P <= 2) or 3 WGs per CU; 5 <= P <= 8: register-direct,
+ *                   4 KiB chunks, unroll 1, <= 4 WGs per CU; P >= 9:
+ *                   register-direct, 4 KiB chunks, unroll 1, <= 3 WGs per CU
  *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
  *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
  *                   two or more: 32 KiB chunks, <= 2 WGs per CU,
@@ -141,7 +139,21 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                cap.  Fewer resident waves keep fewer DRAM pages open at
  *                once, which is what lets P-stream kernels reach the HBM
  *                bandwidth a single copy stream gets.
- *   reserved     must be 0.
+ *   store_policy how the nontemporal stores reach memory: 1 = write-through
+ *                (the stores carry the device-scope bit as well, so the L2
+ *                forwards each line to memory instead of keeping it dirty;
+ *                collectives, reshard copy and fused RMSNorm, for chunks of
+ *                up to 1 GiB), 2 = nontemporal only, 0 = default:
+ *                write-through for all-reduce, reduce-scatter and reduce,
+ *                for all-gather and broadcast at P <= 2 and P = 7, 8, and for
+ *                the row-pipelined fused RMSNorm, each only where every
+ *                output's stores start on a 256-byte boundary (partial lines
+ *                written through cost far more than they save); nontemporal
+ *                only for the other all-gathers and broadcasts, the
+ *                realigning kernel and the reshard copy.  Write-through needs
+ *                >= 4 resident workgroups per CU to cover its longer store
+ *                completion in the all-gather; with fewer it can be much
+ *                slower.  Ignored when nontemporal stores are off.
  */
 typedef struct {
     uint64_t chunk_bytes;
@@ -150,7 +162,7 @@ typedef struct {
     int32_t unroll;
     int32_t nontemporal;
     int32_t occupancy;
-    int32_t reserved;
+    int32_t store_policy;
 } ccl_launch_config_t;
 
 /*

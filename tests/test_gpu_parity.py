@@ -145,6 +145,10 @@ def test_bf16_rounding_ties_exercised():
     dict(unroll=1), dict(unroll=2), dict(unroll=4), dict(stages=2), dict(stages=4),
     dict(nontemporal=1), dict(nontemporal=2), dict(nontemporal=3), dict(nontemporal=4),
     dict(chunk_bytes=4096, workgroups=3, unroll=1, nontemporal=4),
+    dict(store_policy=1), dict(store_policy=2), dict(store_policy=1, occupancy=2),
+    dict(store_policy=1, stages=2), dict(store_policy=1, stages=3, chunk_bytes=8192),
+    dict(store_policy=1, chunk_bytes=1 << 20, workgroups=7), dict(store_policy=1, unroll=4),
+    dict(store_policy=1, nontemporal=1), dict(store_policy=2, stages=2),
 ])
 def test_launch_config_does_not_change_results(cfg):
     P, n = 8, 50001
@@ -337,6 +341,31 @@ def test_lds_pipeline_few_workgroups_and_offsets(cfg):
     want = oracle.all_reduce(xs, "bf16", "sum")
     for off in (0, 6):
         got = run_ar(xs, "bf16", "sum", offset=off, cfg=ccl.LaunchConfig(chunk_bytes=16384, **cfg))
+        for q in range(P):
+            np.testing.assert_array_equal(got[q], want[q])
+
+
+@pytest.mark.parametrize("pol", [1, 2])
+@pytest.mark.parametrize("P", [3, 8, 12])
+def test_store_policies_on_realigned_and_offset_buffers(P, pol):
+    """Write-through and nontemporal-only stores on the realigning kernel
+    (ragged shards, inputs at another offset than outputs) and on buffers
+    whose common offset leaves a scalar head."""
+    cfg = ccl.LaunchConfig(store_policy=pol)
+    m = 1237
+    xr = si.rank_buffers(P, P * m, "bf16", "uniform", seed=P + 40)
+    got = run_rs(xr, "bf16", "sum", offset=2, out_offset=0, cfg=cfg)
+    want = oracle.reduce_scatter(xr, "bf16", "sum")
+    for s in range(P):
+        assert_parity(got[s], want[s], "bf16", "sum", f"RS realigned pol={pol}")
+    xg = si.rank_buffers(P, m, "bf16", "normal", seed=P + 41)
+    got = run_ag(xg, "bf16", offset=6, out_offset=0, cfg=cfg)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
+    xa = si.rank_buffers(P, 5 * m, "f32", "uniform", seed=P + 42)
+    want = oracle.all_reduce(xa, "f32", "max")
+    for off, out_off in ((4, 0), (8, 8)):
+        got = run_ar(xa, "f32", "max", offset=off, out_offset=out_off, cfg=cfg)
         for q in range(P):
             np.testing.assert_array_equal(got[q], want[q])
 

@@ -110,7 +110,10 @@ def test_reshard_launch_config_does_not_change_results(chunk, wgs):
 # every nontemporal choice is its own kernel instantiation
 @pytest.mark.parametrize("cfg", [dict(nontemporal=1), dict(nontemporal=2), dict(nontemporal=4),
                                  dict(nontemporal=4, unroll=1, occupancy=32),
-                                 dict(nontemporal=2, unroll=2, chunk_bytes=8192)])
+                                 dict(nontemporal=2, unroll=2, chunk_bytes=8192),
+                                 dict(store_policy=1), dict(store_policy=2),
+                                 dict(store_policy=1, nontemporal=2, chunk_bytes=1024),
+                                 dict(store_policy=2, nontemporal=3)])
 def test_reshard_nontemporal_variants(cfg):
     shape, src, dst = CASES[8]
     G = si.tensor(shape, "bf16", "w002", seed=98)

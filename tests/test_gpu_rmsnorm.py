@@ -80,7 +80,9 @@ def test_bf16_hidden_16384_and_in_place(cfg):
                                  dict(stages=2, workgroups=1), dict(stages=2, workgroups=39),
                                  dict(stages=2, workgroups=40), dict(stages=2, workgroups=41),
                                  dict(stages=2, occupancy=1), dict(stages=2, occupancy=3),
-                                 dict(stages=2, nontemporal=4)])
+                                 dict(stages=2, nontemporal=4), dict(store_policy=1),
+                                 dict(store_policy=2), dict(stages=2, store_policy=2),
+                                 dict(stages=2, store_policy=1, nontemporal=2)])
 def test_launch_config_does_not_change_results(cfg):
     P, rows, hidden = 8, 40, 4096
     xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=9)

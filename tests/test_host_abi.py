@@ -81,7 +81,8 @@ def test_rejects_bad_scalars(call):
     assert go(recv=[FAKE * 2 + 2] + ptrs(3, base=FAKE * 3)) == E  # misaligned fp32
     for bad in [dict(chunk_bytes=100), dict(chunk_bytes=1000), dict(workgroups=-1),
                 dict(stages=5), dict(unroll=3), dict(unroll=5), dict(nontemporal=5),
-                dict(stages=2, chunk_bytes=1024 * 6)]:
+                dict(stages=2, chunk_bytes=1024 * 6), dict(store_policy=3),
+                dict(store_policy=-1)]:
         assert go(cfg=ccl.LaunchConfig(**bad)) == E, bad
     # count 0 is a no-op that never looks at the pointers
     assert go(count=0, send=[0] * 4, recv=[0] * 4) == ccl.CCL_OK
