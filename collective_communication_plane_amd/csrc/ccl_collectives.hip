@@ -117,21 +117,23 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     if (!l.occupancy_set) occupancy = d.kind != KIND_AG ? (many ? 4 : 8) : d.P <= 6 ? 4 : 3;
     if (!l.nt_set && d.kind == KIND_RS) a.flags &= ~1;
   }
-  p.occupancy = occupancy;
   // Write-through stores by default (measured on MI355X, bf16): +1-6 % for
-  // the all-reduce and the reduce-scatter at every P; +8 % for the
-  // all-gather at P <= 2 and +7-35 % at P = 7, 8 (with >= 4 resident
-  // workgroups per CU), but slower at P = 3, 4.  Only where every chunk's
-  // stores start on a 256-byte boundary: the all-gather at P = 8 with shards
-  // of 2^24 + 8 elements ran 4086 GB/s with them against 5166 without, and
-  // every shard size that is not a multiple of 256 bytes lost 10-43 %.
-  // The realigning kernel keeps nontemporal-only stores.  They address a
-  // chunk through a buffer resource with 31-bit offsets.
+  // the all-reduce and the reduce-scatter at every P; for the all-gather +8 %
+  // at P <= 2, +2-35 % at 5 <= P <= 8 and +2-7 % at P = 12, 16 with >= 4
+  // resident workgroups per CU (with 3 they lose up to 40 %), but not at
+  // P = 3, 4.  Only where every chunk's stores start on a 256-byte boundary:
+  // the all-gather at P = 8 with shards of 2^24 + 8 elements ran 4086 GB/s
+  // with them against 5166 without, and every shard size that is not a
+  // multiple of 256 bytes lost 10-43 %.  The realigning kernel keeps
+  // nontemporal-only stores.  They address a chunk through a buffer resource
+  // with 31-bit offsets.
   bool wt = l.store_wt;
   if (!l.store_pol_set)
-    wt = !realign && lines_aligned &&
-         (d.kind != KIND_AG || d.P <= 2 || (d.P >= 7 && d.P <= 8));
-  if (l.nt_store && wt && chunk_bytes <= (uint64_t(1) << 30)) a.flags |= 4;
+    wt = !realign && lines_aligned && (d.kind != KIND_AG || d.P <= 2 || d.P >= 5);
+  wt = wt && l.nt_store && chunk_bytes <= (uint64_t(1) << 30);
+  if (wt) a.flags |= 4;
+  if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;
+  p.occupancy = occupancy;
   a.chunk_vecs = chunk_bytes / kVecBytes;
   a.chunks_per_seg = std::max<uint64_t>(1, (max_nvec + a.chunk_vecs - 1) / a.chunk_vecs);
   a.total_chunks = a.chunks_per_seg * nseg;

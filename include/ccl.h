@@ -145,8 +145,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                collectives, reshard copy and fused RMSNorm, for chunks of
  *                up to 1 GiB), 2 = nontemporal only, 0 = default:
  *                write-through for all-reduce, reduce-scatter and reduce,
- *                for all-gather and broadcast at P <= 2 and P = 7, 8, and for
- *                the row-pipelined fused RMSNorm, each only where every
+ *                for all-gather and broadcast at P <= 2 and P >= 5 (from
+ *                P = 9 on with <= 4 WGs per CU instead of 3), and for the
+ *                row-pipelined fused RMSNorm, each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
  *                only for the other all-gathers and broadcasts, the
