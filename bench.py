@@ -276,6 +276,7 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"workload": desc, "hbm_bytes": nbytes, "ms": round(ms, 5),
                      "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        print(f"bench: row {name}: {gbs:.1f} GB/s", file=sys.stderr, flush=True)
 
     P, N = 8, 67_108_864
     M = N // P
@@ -604,6 +605,7 @@ def main() -> int:
     torch.cuda.synchronize()
     ms = timed(step, args.steps, args.warmup, stream)
     value = bytes_per_step / (ms * 1e-3) / 1e9
+    print(f"bench: headline all_reduce {value:.1f} GB/s", file=sys.stderr, flush=True)
 
     # spot-check the timed outputs against the oracle
     import oracle

@@ -46,7 +46,8 @@ struct CollArgs {
   uint64_t total_chunks;
   int P;
   // bit 0: nontemporal loads, bit 1: nontemporal stores, bit 2: those stores
-  // write-through (st_wt; the host sets it only for chunks below 2 GiB)
+  // write-through (register-direct kernel only; the host sets it only for
+  // chunks of at most 1 GiB)
   int flags;
 };
 
@@ -145,7 +146,10 @@ struct VecWaves {
 
 // Register-direct kernel.  PMAX bounds P at compile time so every load of a
 // lane's U x P vectors is issued before the first fold.
-template <int KIND, int DT, int OP, int PMAX, int U>
+// WT: write-through stores (st_wt) as a compile-time choice, so that the
+// nontemporal / plain kernel stays exactly what it is without them (a runtime
+// branch among the three store paths slowed the nontemporal one).
+template <int KIND, int DT, int OP, int PMAX, int U, bool WT>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(VecWaves<KIND, PMAX, U>::value)))
     coll_vec_kernel(CollArgs a) {
@@ -156,7 +160,7 @@ __global__ void __launch_bounds__(kThreads)
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
 
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int s = (int)(c / a.chunks_per_seg);
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(kThreads)
           u32x4 y;
           if constexpr (KIND == KIND_AG) y = x[u][0];
           else y = fold_vec<DT, OP, NI>(x[u], ni);
-          if (wts) {
+          if constexpr (WT) {
 #pragma unroll
             for (int q = 0; q < NO; ++q)
               if (q < no) st_wt(ob[q] + v0 * kVecBytes, (vv - v0) * kVecBytes, y);
@@ -262,7 +266,7 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
 
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int s = (int)(c / a.chunks_per_seg);
@@ -337,11 +341,7 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
       u32x4 y;
       if constexpr (KIND == KIND_AG) y = x[0];
       else y = fold_vec<DT, OP, NI>(x, ni);
-      if (wts) {
-#pragma unroll
-        for (int q = 0; q < NO; ++q)
-          if (q < no) st_wt(ob[q] + v0 * kVecBytes, (v - v0) * kVecBytes, y);
-      } else if (nts) {
+      if (nts) {
 #pragma unroll
         for (int q = 0; q < NO; ++q)
           if (q < no) st_nt(ob[q] + v * kVecBytes, y);
@@ -471,7 +471,7 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
+  const bool ntl = a.flags & 1, nts = a.flags & 2;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
@@ -562,10 +562,9 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
 #pragma unroll
         for (int q = 0; q < NO; ++q)
           if (q < no) {
-            char *d = out_at<KIND>(a, s, q, head, esz);
-            if (wts) st_wt(d + k.v0 * kVecBytes, (vv - k.v0) * kVecBytes, y);
-            else if (nts) st_nt(d + vv * kVecBytes, y);
-            else st_plain(d + vv * kVecBytes, y);
+            char *d = out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes;
+            if (nts) st_nt(d, y);
+            else st_plain(d, y);
           }
       }
       cursor_next(a, k);
@@ -583,14 +582,20 @@ inline int lds_stages(int stages, int ni_max) {
 
 // ------------------------------------------------------------- dispatch
 
+template <int KIND, int DT, int OP, int PMAX, bool WT>
+void launch_vec_u(const CollArgs &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
+  if (unroll == 1)
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 1, WT>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (unroll == 2 || PMAX > 8)
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 2, WT>), dim3(grid), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 4, WT>), dim3(grid), dim3(kThreads), lds, st, a);
+}
+
 template <int KIND, int DT, int OP, int PMAX>
 hipError_t launch_vec(const CollArgs &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
-  if (unroll == 1)
-    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 1>), dim3(grid), dim3(kThreads), lds, st, a);
-  else if (unroll == 2 || PMAX > 8)
-    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 2>), dim3(grid), dim3(kThreads), lds, st, a);
-  else
-    hipLaunchKernelGGL((coll_vec_kernel<KIND, DT, OP, PMAX, 4>), dim3(grid), dim3(kThreads), lds, st, a);
+  if (a.flags & 4) launch_vec_u<KIND, DT, OP, PMAX, true>(a, unroll, grid, lds, st);
+  else launch_vec_u<KIND, DT, OP, PMAX, false>(a, unroll, grid, lds, st);
   return hipGetLastError();
 }
 

@@ -117,20 +117,24 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     if (!l.occupancy_set) occupancy = d.kind != KIND_AG ? (many ? 4 : 8) : d.P <= 6 ? 4 : 3;
     if (!l.nt_set && d.kind == KIND_RS) a.flags &= ~1;
   }
-  // Write-through stores by default (measured on MI355X, bf16): +1-6 % for
-  // the all-reduce and the reduce-scatter at every P; for the all-gather +8 %
-  // at P <= 2, +2-35 % at 5 <= P <= 8 and +2-7 % at P = 12, 16 with >= 4
-  // resident workgroups per CU (with 3 they lose up to 40 %), but not at
-  // P = 3, 4.  Only where every chunk's stores start on a 256-byte boundary:
-  // the all-gather at P = 8 with shards of 2^24 + 8 elements ran 4086 GB/s
-  // with them against 5166 without, and every shard size that is not a
-  // multiple of 256 bytes lost 10-43 %.  The realigning kernel keeps
-  // nontemporal-only stores.  They address a chunk through a buffer resource
-  // with 31-bit offsets.
+  // Write-through stores (register-direct kernel only), by default where they
+  // won in same-binary A/B runs on MI355X (bf16, separate kernel
+  // instantiations): the all-gather and broadcast at P = 2 and 4 <= P <= 12
+  // with >= 4 resident workgroups per CU (+5 % to +31 %; with 3 they lose up
+  // to 30 %), not at P = 3 or P >= 13; the reduce-scatter and reduce at
+  // P <= 8 (+3 % at P <= 4, +1.3 % at P = 8; -0.3 to -0.8 % from P = 12).
+  // The all-reduce keeps nontemporal-only stores: its headline layout ran
+  // 3.1 % slower with them.  Only where every chunk's stores start on a
+  // 256-byte boundary: the all-gather at P = 8 with shards of 2^24 + 8
+  // elements ran 4086 GB/s with them against 5166 without, and every shard
+  // size that is not a multiple of 256 bytes lost 10-43 %.  The stores
+  // address a chunk through a buffer resource with 31-bit offsets.
   bool wt = l.store_wt;
   if (!l.store_pol_set)
-    wt = !realign && lines_aligned && (d.kind != KIND_AG || d.P <= 2 || d.P >= 5);
-  wt = wt && l.nt_store && chunk_bytes <= (uint64_t(1) << 30);
+    wt = lines_aligned &&
+         (d.kind == KIND_AG ? (d.P == 2 || (d.P >= 4 && d.P <= 12))
+                            : d.kind == KIND_RS && d.P <= 8);
+  wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;
   p.occupancy = occupancy;

@@ -82,11 +82,12 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
  *                   <= 4 WGs per CU for 9 <= P <= 12; for P = 7, 8 with more
- *                   than 160 MiB per rank, the 2-stage LDS pipeline with <= 2
- *                   WGs per CU
+ *                   than 160 MiB per rank and outputs that do not all start on
+ *                   256 bytes (so no write-through stores), the 2-stage LDS
+ *                   pipeline with <= 2 WGs per CU
  *   broadcast       as all-gather
- *   all-gather      P <= 4: register-direct, 8 KiB chunks, unroll 2, <= 4
- *                   (P <= 2) or 3 WGs per CU; 5 <= P <= 8: register-direct,
+ *   all-gather      P <= 3: register-direct, 8 KiB chunks, unroll 2, <= 4
+ *                   (P <= 2) or 3 WGs per CU; 4 <= P <= 8: register-direct,
  *                   4 KiB chunks, unroll 1, <= 4 WGs per CU; P >= 9:
  *                   register-direct, 4 KiB chunks, unroll 1, <= 3 WGs per CU
  *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
@@ -144,14 +145,16 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                forwards each line to memory instead of keeping it dirty;
  *                collectives, reshard copy and fused RMSNorm, for chunks of
  *                up to 1 GiB), 2 = nontemporal only, 0 = default:
- *                write-through for all-reduce, reduce-scatter and reduce,
- *                for all-gather and broadcast at P <= 2 and P >= 5 (from
+ *                write-through for reduce-scatter and reduce at P <= 8, for
+ *                all-gather and broadcast at P = 2 and 4 <= P <= 12 (from
  *                P = 9 on with <= 4 WGs per CU instead of 3), and for the
  *                row-pipelined fused RMSNorm, each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
- *                only for the other all-gathers and broadcasts, the
- *                realigning kernel and the reshard copy.  Write-through needs
+ *                only for the all-reduce, the other all-gathers and
+ *                broadcasts, the reshard copy and the one-row RMSNorm.
+ *                Write-through applies to the register-direct kernels only
+ *                (not the LDS pipeline or the realigning kernel).  It needs
  *                >= 4 resident workgroups per CU to cover its longer store
  *                completion in the all-gather; with fewer it can be much
  *                slower.  Ignored when nontemporal stores are off.
