@@ -50,6 +50,19 @@ __device__ __forceinline__ void st_wt(char *base, uint64_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolNtSc1);
 }
 
+// The same for 8- and 4-byte stores.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_wt_b64(char *base, uint64_t off, u32x2 v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2 | 16);
+}
+__device__ __forceinline__ void st_wt_b32(char *base, uint64_t off, uint32_t v) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 2 | 16);
+}
+
 // A pointer the caller knows to be the same in every lane, moved to scalar
 // registers so that a buffer resource can be built from it without a loop
 // over lanes.

@@ -48,7 +48,7 @@ inline OpDefaults default_launch(Op op, int P) {
     case OP_RMSNORM:
       return {16384, 1, 1, 0};
     case OP_RESHARD_FP8:
-      return {65536, 1, 2, 0};
+      return {32768, 1, 2, 0};
     default:
       return {32768, 1, 4, 2};
   }

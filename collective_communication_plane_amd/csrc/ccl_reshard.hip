@@ -203,8 +203,8 @@ __device__ __forceinline__ uint32_t e4m3_pack2(float a, float b, uint32_t word) 
 }
 
 // U = 16-byte vectors each lane loads before it processes any of them;
-// NTL / NTS: nontemporal source loads / code stores.
-template <int DT, int U, bool NTL, bool NTS>
+// NTL: nontemporal source loads; SP: store policy of the codes (StorePol).
+template <int DT, int U, bool NTL, int SP>
 __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a) {
   constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
   constexpr int EPL = kVecBytes / esz;             // elements per lane
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
 #pragma unroll
     for (int j = 0; j < kRhoRegs; ++j)
       if (j < a.rho) {
-        cdst[j] = a.codes[rep[j]] + elem0;
+        cdst[j] = wave_uniform(a.codes[rep[j]] + elem0);
         sdst[j] = a.scales[rep[j]] + elem0 / kFp8Block;
       }
     // Whole groups iterate together so shuffles see every lane of a block;
@@ -296,14 +296,15 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
         auto put = [&](char *d, float *sc) {
           if (valid == (uint32_t)EPL) {
             if constexpr (EPL == 8) {
-              typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
               u32x2 w2;
               w2[0] = lo;
               w2[1] = hi;
-              if constexpr (NTS) __builtin_nontemporal_store(w2, (u32x2 *)(d + e_off));
+              if constexpr (SP == ST_WT) st_wt_b64(d, e_off, w2);
+              else if constexpr (SP == ST_NT) __builtin_nontemporal_store(w2, (u32x2 *)(d + e_off));
               else *(u32x2 *)(d + e_off) = w2;
             } else {
-              if constexpr (NTS) __builtin_nontemporal_store(lo, (uint32_t *)(d + e_off));
+              if constexpr (SP == ST_WT) st_wt_b32(d, e_off, lo);
+              else if constexpr (SP == ST_NT) __builtin_nontemporal_store(lo, (uint32_t *)(d + e_off));
               else *(uint32_t *)(d + e_off) = lo;
             }
           } else {
@@ -315,25 +316,32 @@ __global__ void __launch_bounds__(kThreads) reshard_fp8_kernel(ReshardFp8Args a)
         for (int j = 0; j < kRhoRegs; ++j)
           if (j < a.rho) put(cdst[j], sdst[j]);
         for (int j = kRhoRegs; j < a.rho; ++j)
-          put(a.codes[rep[j]] + elem0, a.scales[rep[j]] + elem0 / kFp8Block);
+          put(wave_uniform(a.codes[rep[j]] + elem0), a.scales[rep[j]] + elem0 / kFp8Block);
       }
     }
   }
 }
 
-template <int DT, bool NTL, bool NTS>
+template <int DT, bool NTL, int SP>
 void launch_fp8_u(const ReshardFp8Args &a, int unroll, unsigned grid, size_t lds, hipStream_t st) {
-  if (unroll >= 4) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 4, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-  else if (unroll == 2) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 2, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
-  else hipLaunchKernelGGL((reshard_fp8_kernel<DT, 1, NTL, NTS>), dim3(grid), dim3(kThreads), lds, st, a);
+  if (unroll >= 4) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 4, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+  else if (unroll == 2) hipLaunchKernelGGL((reshard_fp8_kernel<DT, 2, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL((reshard_fp8_kernel<DT, 1, NTL, SP>), dim3(grid), dim3(kThreads), lds, st, a);
 }
 
 template <int DT>
 void launch_fp8_dt(const ReshardFp8Args &a, const Launch &l, unsigned grid, size_t lds, hipStream_t st) {
-  if (l.nt_load && l.nt_store) launch_fp8_u<DT, true, true>(a, l.unroll, grid, lds, st);
-  else if (l.nt_load) launch_fp8_u<DT, true, false>(a, l.unroll, grid, lds, st);
-  else if (l.nt_store) launch_fp8_u<DT, false, true>(a, l.unroll, grid, lds, st);
-  else launch_fp8_u<DT, false, false>(a, l.unroll, grid, lds, st);
+  // code stores: write-through only when the caller asks for it
+  const int sp = !l.nt_store ? ST_PLAIN : (l.store_pol_set && l.store_wt) ? ST_WT : ST_NT;
+  if (l.nt_load) {
+    if (sp == ST_WT) launch_fp8_u<DT, true, ST_WT>(a, l.unroll, grid, lds, st);
+    else if (sp == ST_NT) launch_fp8_u<DT, true, ST_NT>(a, l.unroll, grid, lds, st);
+    else launch_fp8_u<DT, true, ST_PLAIN>(a, l.unroll, grid, lds, st);
+  } else {
+    if (sp == ST_WT) launch_fp8_u<DT, false, ST_WT>(a, l.unroll, grid, lds, st);
+    else if (sp == ST_NT) launch_fp8_u<DT, false, ST_NT>(a, l.unroll, grid, lds, st);
+    else launch_fp8_u<DT, false, ST_PLAIN>(a, l.unroll, grid, lds, st);
+  }
 }
 
 // Build (or find) the device copy of the plan for this device and chunk size.

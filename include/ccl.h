@@ -94,7 +94,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
  *                   two or more: 32 KiB chunks, <= 2 WGs per CU,
  *                   nontemporal stores only
- *   reshard + fp8   64 KiB chunks, unroll 2, no cap (the quantizing pass does
+ *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  rows of up to 16 KiB per rank: one workgroup per
  *                   row; <= 3 WGs per CU for rows of 4-8 KiB, otherwise
@@ -143,8 +143,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   store_policy how the nontemporal stores reach memory: 1 = write-through
  *                (the stores carry the device-scope bit as well, so the L2
  *                forwards each line to memory instead of keeping it dirty;
- *                collectives, reshard copy and fused RMSNorm, for chunks of
- *                up to 1 GiB), 2 = nontemporal only, 0 = default:
+ *                collectives, reshard copy, FP8 reshard codes and fused
+ *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
+ *                0 = default:
  *                write-through for reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2 and 4 <= P <= 12 (from
  *                P = 9 on with <= 4 WGs per CU instead of 3), and for the
@@ -152,7 +153,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
  *                only for the all-reduce, the other all-gathers and
- *                broadcasts, the reshard copy and the one-row RMSNorm.
+ *                broadcasts, the reshard copy, the FP8 reshard (+1.3 % with
+ *                write-through, within noise) and the one-row RMSNorm.
  *                Write-through applies to the register-direct kernels only
  *                (not the LDS pipeline or the realigning kernel).  It needs
  *                >= 4 resident workgroups per CU to cover its longer store

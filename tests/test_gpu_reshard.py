@@ -404,7 +404,10 @@ def _fp8_variant_case(dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("cfg", [dict(unroll=1), dict(unroll=4), dict(nontemporal=1),
                                  dict(nontemporal=2), dict(nontemporal=4, unroll=1),
-                                 dict(chunk_bytes=1024, workgroups=3), dict(occupancy=2)])
+                                 dict(chunk_bytes=1024, workgroups=3), dict(occupancy=2),
+                                 dict(store_policy=1), dict(store_policy=1, unroll=4),
+                                 dict(store_policy=1, chunk_bytes=1024, workgroups=3),
+                                 dict(store_policy=2), dict(store_policy=1, nontemporal=1)])
 def test_reshard_fp8_launch_variants(cfg, dtype):
     shape, src, dst = FP8_CASES[1]
     src_bufs, want = _fp8_variant_case(dtype)
