@@ -119,21 +119,26 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   }
   // Write-through stores (register-direct kernel only), by default where they
   // won in same-binary A/B runs on MI355X (bf16, separate kernel
-  // instantiations): the all-gather and broadcast at P = 2 and 4 <= P <= 12
-  // with >= 4 resident workgroups per CU (+5 % to +31 %; with 3 they lose up
-  // to 30 %), not at P = 3 or P >= 13; the reduce-scatter and reduce at
-  // P <= 8 (+3 % at P <= 4, +1.3 % at P = 8; -0.3 to -0.8 % from P = 12).
-  // The all-reduce keeps nontemporal-only stores: its headline layout ran
-  // 3.1 % slower with them.  Only where every chunk's stores start on a
-  // 256-byte boundary: the all-gather at P = 8 with shards of 2^24 + 8
-  // elements ran 4086 GB/s with them against 5166 without, and every shard
-  // size that is not a multiple of 256 bytes lost 10-43 %.  The stores
-  // address a chunk through a buffer resource with 31-bit offsets.
+  // instantiations): the reduce-scatter and reduce at P <= 8 (+3 % at P <= 4,
+  // +1-8 % at P = 7, 8 from 64 to 512 MiB per rank; -0.3 to -0.8 % from
+  // P = 12); the all-gather and broadcast at P = 2 (+7 %) and, with >= 4
+  // resident workgroups per CU, at 4 <= P <= 12 when the whole input fits
+  // the 256 MiB MALL (+5 % to +30 %: written-through lines leave the input
+  // cached between calls; with 341-512 MiB of input they lose 2-6 %, at P = 3
+  // and P >= 13 they lose, with 3 workgroups per CU up to 30 %).  The
+  // all-reduce keeps nontemporal-only stores: its headline layout ran 3.1 %
+  // slower with them.  Only where every chunk's stores start on a 256-byte
+  // boundary: the all-gather at P = 8 with shards of 2^24 + 8 elements ran
+  // 4086 GB/s with them against 5166 without, and every shard size that is
+  // not a multiple of 256 bytes lost 10-43 %.  The stores address a chunk
+  // through a buffer resource with 31-bit offsets.
+  const uint64_t ag_in_bytes = (uint64_t)(d.single ? 1 : d.P) * M * esz;
   bool wt = l.store_wt;
   if (!l.store_pol_set)
     wt = lines_aligned &&
-         (d.kind == KIND_AG ? (d.P == 2 || (d.P >= 4 && d.P <= 12))
-                            : d.kind == KIND_RS && d.P <= 8);
+         (d.kind == KIND_AG
+              ? (d.P == 2 || (d.P >= 4 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)))
+              : d.kind == KIND_RS && d.P <= 8);
   wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;

@@ -147,8 +147,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
  *                write-through for reduce-scatter and reduce at P <= 8, for
- *                all-gather and broadcast at P = 2 and 4 <= P <= 12 (from
- *                P = 9 on with <= 4 WGs per CU instead of 3), and for the
+ *                all-gather and broadcast at P = 2, and at 4 <= P <= 12 with
+ *                at most 256 MiB of input in all (from P = 9 on with <= 4 WGs
+ *                per CU instead of 3), and for the
  *                row-pipelined fused RMSNorm, each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
