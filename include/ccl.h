@@ -146,14 +146,15 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                collectives, reshard copy, FP8 reshard codes and fused
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
- *                write-through for reduce-scatter and reduce at P <= 8, for
+ *                write-through for the all-reduce at P = 8 with more than
+ *                256 MiB per rank, for reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, and at 4 <= P <= 12 with
  *                at most 256 MiB of input in all (from P = 9 on with <= 4 WGs
  *                per CU instead of 3), and for the
  *                row-pipelined fused RMSNorm, each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
- *                only for the all-reduce, the other all-gathers and
+ *                only for the other all-reduces, the other all-gathers and
  *                broadcasts, the reshard copy, the FP8 reshard (+1.3 % with
  *                write-through, within noise) and the one-row RMSNorm.
  *                Write-through applies to the register-direct kernels only
