@@ -146,9 +146,12 @@ def test_all_reduce_rmsnorm_past_4gib_per_rank():
 @pytest.mark.parametrize("P", [7, 8, 12])
 def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
     """At P = 7, 8 reduce-scatter and reduce switch from the register-direct
-    kernel to the LDS pipeline past 160 MiB per rank (P = 12 stays
-    register-direct with its own defaults); both sides of that size must give
-    the oracle's values (sum, sampled)."""
+    kernel to the LDS pipeline past 160 MiB per rank when write-through stores
+    do not apply (P = 12 stays register-direct with its own defaults).  These
+    torch tensors start on 256 bytes, so the defaults stay register-direct with
+    write-through stores; the LDS pipeline runs as the forced launch
+    (stages = 2) and the nontemporal-only one as store_policy = 2.  Every form
+    on both sides of that size must give the oracle's values (sum, sampled)."""
     TORCH = {"bf16": torch.int16, "f32": torch.int32}
     for dtype, per_rank_mib in (("bf16", 144), ("bf16", 176), ("f32", 168)):
         esz = 2 if dtype == "bf16" else 4
@@ -161,6 +164,12 @@ def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
         code = ccl.CCL_BFLOAT16 if dtype == "bf16" else ccl.CCL_FLOAT32
         ccl.check(ccl.ccl_reduce_scatter(dx, dy, P, M, code, ccl.CCL_SUM,
                                          torch.cuda.current_stream()), "reduce_scatter")
+        forced = {}
+        for name, cfg in (("lds", ccl.LaunchConfig(stages=2, chunk_bytes=8192)),
+                          ("nt", ccl.LaunchConfig(store_policy=2))):
+            forced[name] = [torch.empty(M, dtype=dx[0].dtype, device=DEV) for _ in range(P)]
+            ccl.check(ccl.ccl_reduce_scatter(dx, forced[name], P, M, code, ccl.CCL_SUM,
+                                             torch.cuda.current_stream(), cfg), "reduce_scatter")
         red = torch.empty(P * M, dtype=dx[0].dtype, device=DEV)
         ccl.check(ccl.ccl_reduce(dx, red, P, P * M, code, ccl.CCL_SUM, P - 1,
                                  torch.cuda.current_stream()), "reduce")
@@ -183,5 +192,7 @@ def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
                 got, got_red = got.view(np.float32), got_red.view(np.float32)
             assert_parity(got, want, dtype, "sum", f"RS P={P} {dtype} {per_rank_mib} MiB shard {s}")
             assert_parity(got_red, want, dtype, "sum", f"reduce P={P} {dtype} {per_rank_mib} MiB")
-        del dx, dy, red
+            for name, ys in forced.items():
+                assert torch.equal(ys[s], dy[s]), f"RS {name} P={P} {dtype} shard {s}"
+        del dx, dy, red, forced
         torch.cuda.empty_cache()

@@ -206,8 +206,9 @@ def test_reduce_scatter_unaligned_and_mixed():
             assert_parity(got[s], want[s], "bf16", "sum", f"RS offsets {off}/{ooff}")
 
 
-def test_reduce_scatter_in_place_nccl_form():
-    P, m = 8, 4099
+@pytest.mark.parametrize("m", [4099, 4096])
+def test_reduce_scatter_in_place_nccl_form(m):
+    P = 8
     xs = si.rank_buffers(P, P * m, "f32", "uniform", seed=9)
     bufs = upload_all(xs, DEV)
     send = [b.ptr for b in bufs]
@@ -255,8 +256,11 @@ def test_all_gather_unaligned_and_mixed():
             np.testing.assert_array_equal(got[q], want[q])
 
 
-def test_all_gather_in_place_nccl_form():
-    P, m = 8, 5000
+# m = 4096 makes every shard a whole number of 256-byte lines, so the default
+# launch takes write-through stores; m = 5000 does not
+@pytest.mark.parametrize("m", [5000, 4096])
+def test_all_gather_in_place_nccl_form(m):
+    P = 8
     xs = si.rank_buffers(P, m, "bf16", "normal", seed=11)
     outs = [DevBuf(P * m * 2, DEV) for _ in range(P)]
     for r in range(P):  # rank r's contribution sits in its own slot of its output
@@ -343,6 +347,26 @@ def test_lds_pipeline_few_workgroups_and_offsets(cfg):
         got = run_ar(xs, "bf16", "sum", offset=off, cfg=ccl.LaunchConfig(chunk_bytes=16384, **cfg))
         for q in range(P):
             np.testing.assert_array_equal(got[q], want[q])
+
+
+@pytest.mark.parametrize("P", [2, 4, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "i32"])
+def test_default_write_through_on_line_aligned_shards(P, dtype):
+    """Shards of whole 256-byte lines take the write-through stores by default
+    (reduce-scatter up to P = 8, all-gather at P = 2 and 4..12); results equal
+    the oracle and the nontemporal-only launch bit for bit."""
+    m = 3 * 4096 // ESZ[dtype]
+    xr = si.rank_buffers(P, P * m, dtype, dist_of(dtype), seed=P + 60)
+    want = oracle.reduce_scatter(xr, dtype, "sum")
+    got = run_rs(xr, dtype, "sum")
+    nt = run_rs(xr, dtype, "sum", cfg=ccl.LaunchConfig(store_policy=2))
+    for s in range(P):
+        assert_parity(got[s], want[s], dtype, "sum", f"RS write-through P={P}")
+        np.testing.assert_array_equal(got[s], nt[s])
+    xg = si.rank_buffers(P, m, dtype, dist_of(dtype), seed=P + 61)
+    got = run_ag(xg, dtype)
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], np.concatenate(xg))
 
 
 @pytest.mark.parametrize("pol", [1, 2])
