@@ -126,9 +126,10 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // the 256 MiB MALL (+5 % to +30 %: written-through lines leave the input
   // cached between calls; with 341-512 MiB of input they lose 2-6 %, at P = 3
   // and P >= 13 they lose, with 3 workgroups per CU up to 30 %); the
-  // all-reduce only at P = 8 with more than 256 MiB per rank (+1-7.5 % at
-  // 384 MiB to 1 GiB, where the footprint is past 4 GiB; -2.5 to -7 % at
-  // 128-256 MiB, and no consistent sign at other P).  Only where every
+  // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank (P = 8:
+  // +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at 128-256 MiB; P = 3-6 with
+  // 341-682 MiB per rank: +2-11 % over the defaults, P = 3, 4 with 8 KiB
+  // chunks and <= 3 workgroups per CU).  Only where every
   // chunk's stores start on a 256-byte boundary: the all-gather at P = 8 with
   // shards of 2^24 + 8 elements ran 4086 GB/s with them against 5166 without,
   // and every shard size that is not a multiple of 256 bytes lost 10-43 %.
@@ -140,10 +141,14 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
          (d.kind == KIND_AG
               ? (d.P == 2 || (d.P >= 4 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
-                              : d.P == 8 && M * esz > (uint64_t(256) << 20));
+                              : d.P >= 3 && d.P <= 8 && M * esz > (uint64_t(256) << 20));
   wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;
+  if (wt && d.kind == KIND_AR && d.P <= 4) {
+    if (!l.chunk_set) chunk_bytes = 8192;
+    if (!l.occupancy_set) occupancy = 3;
+  }
   p.occupancy = occupancy;
   a.chunk_vecs = chunk_bytes / kVecBytes;
   a.chunks_per_seg = std::max<uint64_t>(1, (max_nvec + a.chunk_vecs - 1) / a.chunk_vecs);

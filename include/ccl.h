@@ -146,8 +146,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                collectives, reshard copy, FP8 reshard codes and fused
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
- *                write-through for the all-reduce at P = 8 with more than
- *                256 MiB per rank, for reduce-scatter and reduce at P <= 8, for
+ *                write-through for the all-reduce at 3 <= P <= 8 with more
+ *                than 256 MiB per rank (at P = 3, 4 with 8 KiB chunks and
+ *                <= 3 WGs per CU), for reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, and at 4 <= P <= 12 with
  *                at most 256 MiB of input in all (from P = 9 on with <= 4 WGs
  *                per CU instead of 3), and for the
