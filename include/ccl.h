@@ -77,7 +77,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  * which come from that sweep on MI355X (2 GiB of bf16 input over P ranks):
  *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
  *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
- *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU;
+ *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
+ *                   write-through stores, past 256 MiB per rank: 8 KiB
+ *                   chunks, <= 3 WGs per CU);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
@@ -90,6 +92,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   (P <= 2) or 3 WGs per CU; 4 <= P <= 8: register-direct,
  *                   4 KiB chunks, unroll 1, <= 4 WGs per CU; P >= 9:
  *                   register-direct, 4 KiB chunks, unroll 1, <= 3 WGs per CU
+ *                   (<= 4 with write-through stores)
  *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
  *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
  *                   two or more: 32 KiB chunks, <= 2 WGs per CU,
