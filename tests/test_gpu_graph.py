@@ -121,3 +121,43 @@ def test_fused_and_reshard_calls_in_a_graph():
     finally:
         torch.cuda.synchronize()
         ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+def test_write_through_calls_in_a_graph():
+    """Write-through stores (buffer stores with the device-scope bit) replay
+    bit-identically from a graph: the all-gather on line-aligned shards and
+    the row-pipelined RMSNorm by default, the all-reduce, reshard copy and FP8
+    codes by request."""
+    P, n, m = 8, 65536, 8192
+    wt = ccl.LaunchConfig(store_policy=1)
+    x_ar = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    y_ar = [torch.empty_like(t) for t in x_ar]
+    x_ag = [torch.empty(m, dtype=torch.float32, device=DEV) for _ in range(P)]
+    y_ag = [torch.empty(P * m, dtype=torch.float32, device=DEV) for _ in range(P)]
+    rows, hidden = 9, 16384
+    x_n = [torch.empty(rows * hidden, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    y_n = [torch.empty_like(t) for t in x_n]
+    gamma = torch.empty(hidden, dtype=torch.bfloat16, device=DEV)
+    shape = (64, 384)
+    src = [torch.empty(16 * 384, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    dst = [torch.empty(32 * 384, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    codes = [torch.empty(32 * 384, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    scales = [torch.empty(32 * 384 // 128, dtype=torch.float32, device=DEV) for _ in range(4)]
+    st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
+                                    ccl.make_mesh([1, 4], 0), ccl.make_placements(["R", ("S", 0)]),
+                                    ccl.make_mesh([2, 2], 4), ccl.make_placements(["R", ("S", 0)]))
+    ccl.check(st, "reshard_plan")
+    try:
+        def calls(stream):
+            ccl.check(ccl.ccl_all_reduce(x_ar, y_ar, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream, wt))
+            ccl.check(ccl.ccl_all_gather(x_ag, y_ag, P, m, ccl.CCL_FLOAT32, stream))
+            ccl.check(ccl.ccl_all_reduce_rmsnorm(x_n, y_n, P, rows, hidden, gamma, 1e-6,
+                                                 ccl.CCL_BFLOAT16, stream))
+            ccl.check(ccl.ccl_reshard_copy(plan, src, dst, stream, wt))
+            ccl.check(ccl.ccl_reshard_copy_fp8(plan, src, codes, scales, stream, wt))
+
+        _check_replays(calls, x_ar + x_ag + x_n + [gamma] + src,
+                       y_ar + y_ag + y_n + dst + codes + scales)
+    finally:
+        torch.cuda.synchronize()
+        ccl.check(ccl.ccl_plan_destroy(plan))
