@@ -129,11 +129,11 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank (P = 8:
   // +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at 128-256 MiB; P = 3-6 with
   // 341-682 MiB per rank: +2-11 % over the defaults, P = 3, 4 with 8 KiB
-  // chunks and <= 3 workgroups per CU).  Only where every
-  // chunk's stores start on a 256-byte boundary: the all-gather at P = 8 with
-  // shards of 2^24 + 8 elements ran 4086 GB/s with them against 5166 without,
-  // and every shard size that is not a multiple of 256 bytes lost 10-43 %.
-  // The stores address a chunk through a buffer resource with 31-bit offsets.
+  // chunks and <= 3 workgroups per CU).  Only where every chunk's stores
+  // start on a 256-byte boundary: the all-gather at P = 8 with shards of
+  // 2^24 + 8 elements ran 4086 GB/s with them against 5166 without, and every
+  // shard size that is not a multiple of 256 bytes lost 10-43 %.  The stores
+  // address a chunk through a buffer resource with 31-bit offsets.
   const uint64_t ag_in_bytes = (uint64_t)(d.single ? 1 : d.P) * M * esz;
   bool wt = l.store_wt;
   if (!l.store_pol_set)

@@ -34,33 +34,32 @@ __device__ __forceinline__ void st(char *p, u32x4 v) {
   else st_plain(p, v);
 }
 
-// Write-through streaming store: a buffer store with the nontemporal and
+// Write-through streaming stores: buffer stores with the nontemporal and
 // device-scope (sc1) cache-policy bits.  At device scope the L2 of the issuing
-// XCD passes the line on to memory instead of holding it dirty, which on
-// MI355X streams 2-4 % more bytes per second through an all-reduce and up to
-// 8 % through an all-gather at the same launch shape (it needs >= 4 resident
-// workgroups per CU to cover its longer completion time).  The buffer
+// XCD passes the line on to memory instead of holding it dirty.  Whether that
+// is faster depends on the call (the launch code picks it per collective, P
+// and size from measurements); it needs >= 4 resident workgroups per CU to
+// cover its longer completion time, and whole 256-byte lines.  The buffer
 // resource is built from `base`, which the callers keep uniform across the
-// workgroup (a per-lane base would make the compiler loop over lanes); the
-// lane's byte offset from it is below 2^31.
-__device__ __forceinline__ void st_wt(char *base, uint64_t off, u32x4 v) {
-  constexpr int kPolNtSc1 = 2 | 16;  // nt | sc1
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kPolNtSc1);
-}
+// workgroup (a per-lane base would make the compiler loop over lanes): no
+// stride, 2^31 - 1 bytes in range (the lane's byte offset from `base` is
+// below 2^31), and the 32-bit data format that raw buffer accesses on
+// gfx9-family parts take in the resource's last dword.
+constexpr int kPolNtSc1 = 2 | 16;         // cache-policy bits: nt | sc1
+constexpr int kRawBufferWord3 = 0x00020000;
 
-// The same for 8- and 4-byte stores.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wt_rsrc(char *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, kRawBufferWord3);
+}
+__device__ __forceinline__ void st_wt(char *base, uint64_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, wt_rsrc(base), (int)off, 0, kPolNtSc1);
+}
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st_wt_b64(char *base, uint64_t off, u32x2 v) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 2 | 16);
+  __builtin_amdgcn_raw_buffer_store_b64(v, wt_rsrc(base), (int)off, 0, kPolNtSc1);
 }
 __device__ __forceinline__ void st_wt_b32(char *base, uint64_t off, uint32_t v) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 2 | 16);
+  __builtin_amdgcn_raw_buffer_store_b32(v, wt_rsrc(base), (int)off, 0, kPolNtSc1);
 }
 
 // A pointer the caller knows to be the same in every lane, moved to scalar
