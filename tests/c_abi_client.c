@@ -118,6 +118,22 @@ int main(void) {
     /* zero elements is a no-op that succeeds */
     CHECK(ccl_all_reduce(send, recv, 2, 0, CCL_BFLOAT16, CCL_MAX, NULL, NULL) == CCL_OK);
 
+    /* launch configuration: store_policy 0..2 accepted, anything else rejected */
+    {
+        ccl_launch_config_t cfg;
+        memset(&cfg, 0, sizeof cfg);
+        cfg.store_policy = 1;
+        CHECK(ccl_all_reduce(send, recv, 2, 0, CCL_BFLOAT16, CCL_SUM, NULL, &cfg) == CCL_OK);
+        cfg.store_policy = 2;
+        CHECK(ccl_all_gather(send, recv, 2, 0, CCL_BFLOAT16, NULL, &cfg) == CCL_OK);
+        cfg.store_policy = 3;
+        CHECK(ccl_all_reduce(send, recv, 2, 0, CCL_BFLOAT16, CCL_SUM, NULL, &cfg) ==
+              CCL_ERR_INVALID_ARG);
+        cfg.store_policy = -1;
+        CHECK(ccl_reduce_scatter(send, recv, 2, 0, CCL_FLOAT32, CCL_SUM, NULL, &cfg) ==
+              CCL_ERR_INVALID_ARG);
+    }
+
     check_example_a();
     if (failures) return 1;
     printf("ok\n");
