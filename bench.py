@@ -36,6 +36,9 @@ Other modes:
                 fp32 and bf16, sum / min / max: per-call median / min / max of
                 host-issued calls, and the per-call median of 20 calls replayed
                 from one HIP graph (no host work per call).
+  --stores      the library default next to write-through (store_policy 1) and
+                nontemporal-only (2) stores on the bench workloads and the
+                sizes that set the write-through defaults; one JSON line each.
   --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
                 16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
                 same kernel), with the default and an uncapped occupancy, next
@@ -491,6 +494,111 @@ def streams(dev, stream) -> None:
         torch.cuda.empty_cache()
 
 
+def stores(dev, stream) -> None:
+    """Store policies side by side on the bench workloads and the sizes that set the
+    write-through defaults: for each, the library default and store_policy 1
+    (write-through) and 2 (nontemporal only), three interleaved repeats, best
+    GB/s of algorithmic bytes; one JSON line each."""
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    def ab(name, fn, nbytes, extra=()):
+        cfgs = [("default", None), ("write_through", ccl.LaunchConfig(store_policy=1)),
+                ("nontemporal", ccl.LaunchConfig(store_policy=2))] + list(extra)
+        best = {}
+        for _ in range(3):
+            for tag, c in cfgs:
+                ms = timed(lambda: ccl.check(fn(c), name), 30, 20, stream, 0.05)
+                best[tag] = max(best.get(tag, 0.0), nbytes / (ms * 1e-3) / 1e9)
+        print(json.dumps({"stores": name, **{k: round(v, 1) for k, v in best.items()}}), flush=True)
+
+    def bufs(P, nbytes):
+        return [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(P)]
+
+    P = 8
+    for per_rank in (256 << 20, 1 << 30):  # the headline, and past the all-reduce's 256 MiB rule
+        n = per_rank // 2
+        x, _ = rank_slab(P, per_rank, dev)
+        y, _ = rank_slab(P, per_rank, dev)
+        for b in x:
+            b.view(torch.bfloat16).uniform_(-1, 1)
+        ab(f"all_reduce P=8 x {per_rank >> 20} MiB bf16, staggered slabs",
+           lambda c: ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream, c),
+           2 * P * per_rank)
+        del x, y
+        torch.cuda.empty_cache()
+    P, n = 4, (512 << 20) // 2
+    x, y = bufs(P, 2 * n), bufs(P, 2 * n)
+    for b in x:
+        b.view(torch.bfloat16).uniform_(-1, 1)
+    ab("all_reduce P=4 x 512 MiB bf16, one tensor per rank",
+       lambda c: ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream, c), 4 * P * n)
+    del x, y
+    torch.cuda.empty_cache()
+    P, N = 8, 67_108_864
+    lds = ("lds_pipeline", ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=2))
+    for dt, dist, code, esz in [("bf16", "normal", ccl.CCL_BFLOAT16, 2),
+                                ("i32", "int20", ccl.CCL_INT32, 4)]:
+        dx = si.device_rank_buffers(P, N, dt, dist, seed=0, device=dev)
+        dy = [torch.empty(N // P * esz, dtype=torch.uint8, device=dev) for _ in range(P)]
+        ab(f"reduce_scatter P=8 x 67,108,864 {dt}",
+           lambda c: ccl.ccl_reduce_scatter(dx, dy, P, N // P, code, ccl.CCL_SUM, stream, c),
+           P * N * esz + N * esz, [lds])
+        del dx, dy
+        torch.cuda.empty_cache()
+    M = 16_777_216
+    dx = si.device_rank_buffers(P, M, "bf16", "normal", seed=0, device=dev)
+    dy = bufs(P, P * M * 2)
+    ab("all_gather P=8 x 16,777,216 bf16", lambda c: ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, stream, c),
+       P * M * 2 * (1 + P), [("lds_pipeline", ccl.LaunchConfig(stages=2, chunk_bytes=4096, occupancy=3))])
+    del dx, dy
+    torch.cuda.empty_cache()
+    n = (256 << 20) // 2
+    x, y1, ys = bufs(P, 2 * n), bufs(1, 2 * n), bufs(P, 2 * n)
+    for b in x:
+        b.view(torch.bfloat16).uniform_(-1, 1)
+    ab("reduce P=8 x 256 MiB bf16",
+       lambda c: ccl.ccl_reduce(x, y1[0], P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, 0, stream, c), 2 * n * (P + 1))
+    ab("broadcast P=8 x 256 MiB bf16",
+       lambda c: ccl.ccl_broadcast(x[0], ys, P, n, ccl.CCL_BFLOAT16, 0, stream, c), 2 * n * (P + 1))
+    del x, y1, ys
+    torch.cuda.empty_cache()
+    shape = (8192, 28672)
+    G = si.tensor(shape, "bf16", "w002", seed=0)
+    dsrc = [up(np.ascontiguousarray(b), dev) for b in np.split(G, 4, axis=0)]
+    del G
+    tb = sum(t.numel() for t in dsrc)
+    ddst = bufs(4, tb * 2 // 4)
+    st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
+                                    ccl.make_mesh([1, 4], 0), ccl.make_placements(["R", ("S", 0)]),
+                                    ccl.make_mesh([2, 2], 4), ccl.make_placements(["R", ("S", 0)]))
+    ccl.check(st, "reshard_plan")
+    ab("reshard [8192, 28672] TP4 -> TP2 x DP2", lambda c: ccl.ccl_reshard_copy(plan, dsrc, ddst, stream, c),
+       tb * 3)
+    n_local = tb * 2 // 4 // 2
+    codes = bufs(4, n_local)
+    scales = [torch.empty(n_local // 128, dtype=torch.float32, device=dev) for _ in range(4)]
+    ab("reshard [8192, 28672] + FP8", lambda c: ccl.ccl_reshard_copy_fp8(plan, dsrc, codes, scales, stream, c),
+       tb + 4 * (n_local + n_local // 128 * 4))
+    ccl.check(ccl.ccl_plan_destroy(plan))
+    del dsrc, ddst, codes, scales
+    torch.cuda.empty_cache()
+    for rows, hidden in ((16384, 8192), (8192, 16384)):
+        dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=dev)
+        dy = [torch.empty_like(t) for t in dx]
+        gamma = torch.from_numpy(si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
+                                 .view(np.int16).copy()).to(dev)
+        ab(f"all_reduce_rmsnorm P=8 x {rows} x {hidden} bf16",
+           lambda c: ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, gamma, 1e-6,
+                                                ccl.CCL_BFLOAT16, stream, c),
+           2 * P * rows * hidden * 2 + hidden * 2)
+        del dx, dy
+        torch.cuda.empty_cache()
+
+
 def sizes(dev, stream) -> None:
     """All-reduce at P=8 over per-rank sizes 4 KiB * 4^k (k = 0..9, up to 1 GiB),
     fp32 and bf16, sum / min / max, library defaults, ranks in staggered slabs;
@@ -559,6 +667,7 @@ def main() -> int:
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--streams", action="store_true")
     ap.add_argument("--sizes", action="store_true")
+    ap.add_argument("--stores", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -586,6 +695,9 @@ def main() -> int:
         return 0
     if args.sizes:
         sizes(dev, stream)
+        return 0
+    if args.stores:
+        stores(dev, stream)
         return 0
     if args.calibrate:
         calibrate(dev)

@@ -154,13 +154,12 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                <= 3 WGs per CU), for reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, and at 4 <= P <= 12 with
  *                at most 256 MiB of input in all (from P = 9 on with <= 4 WGs
- *                per CU instead of 3), and for the
- *                row-pipelined fused RMSNorm, each only where every
+ *                per CU instead of 3), each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
  *                only for the other all-reduces, the other all-gathers and
- *                broadcasts, the reshard copy, the FP8 reshard (+1.3 % with
- *                write-through, within noise) and the one-row RMSNorm.
+ *                broadcasts, the reshard copy, the FP8 reshard and the fused
+ *                RMSNorm (within +-1.3 % of write-through, either sign).
  *                Write-through applies to the register-direct kernels only
  *                (not the LDS pipeline or the realigning kernel).  It needs
  *                >= 4 resident workgroups per CU to cover its longer store
