@@ -144,6 +144,10 @@ struct PlanInterval {
 struct DevicePlanCache {
   int device = -1;
   void *table = nullptr;  // device copy of the interval, replica and chunk tables
+  void *staging = nullptr;  // pinned host copy the upload reads (lives with the plan)
+  hipEvent_t uploaded = nullptr;  // recorded on the uploading stream after the copy
+  hipStream_t upload_stream = nullptr;
+  bool upload_done = false;       // the event has been seen complete
   size_t rep_offset = 0;       // byte offset of the replica table
   size_t chunk_iv_offset = 0;  // byte offset of the chunk -> interval table (0: none)
   uint64_t chunk_bytes = 0;

@@ -344,55 +344,88 @@ void launch_fp8_dt(const ReshardFp8Args &a, const Launch &l, unsigned grid, size
   }
 }
 
-// Build (or find) the device copy of the plan for this device and chunk size.
-ccl_status_t device_table(ccl_plan *p, int dev, uint64_t chunk_bytes, DevicePlanCache *out) {
+// Build (or find) the device copy of the plan for this device and chunk size,
+// ordered on `stream`.  The first call for a (device, chunk size) fills a
+// pinned host staging buffer that the plan keeps, allocates the device table
+// and enqueues the copy on the caller's stream with an event behind it; the
+// host does not wait.  A later call on another stream waits for that event on
+// its own stream (hipStreamWaitEvent) until the event has been seen complete,
+// so no stream can run a copy kernel over a table still in flight.
+ccl_status_t device_table(ccl_plan *p, int dev, uint64_t chunk_bytes, hipStream_t stream,
+                          DevicePlanCache *out) {
   std::lock_guard<std::mutex> lock(p->mu);
-  for (const auto &e : p->dev)
+  for (auto &e : p->dev)
     if (e.device == dev && e.chunk_bytes == chunk_bytes) {
+      if (!e.upload_done) {
+        const hipError_t q = hipEventQuery(e.uploaded);
+        if (q == hipSuccess) {
+          e.upload_done = true;
+        } else if (q != hipErrorNotReady) {
+          return CCL_ERR_HIP;
+        } else if (stream != e.upload_stream &&
+                   hipStreamWaitEvent(stream, e.uploaded, 0) != hipSuccess) {
+          return CCL_ERR_HIP;
+        }
+      }
       *out = e;
       return CCL_OK;
     }
   const size_t n = p->intervals.size();
   const int rho = p->n_dst / p->n_dst_shards;
-  std::vector<DevInterval> host(n);
   uint64_t chunk = 0;
-  for (size_t i = 0; i < n; ++i) {
-    const PlanInterval &iv = p->intervals[i];
-    host[i] = DevInterval{iv.src_off, iv.dst_off, iv.len, chunk, iv.src_local, iv.dst_shard};
-    chunk += (iv.len + chunk_bytes - 1) / chunk_bytes;
-  }
-  std::vector<int32_t> rep((size_t)p->n_dst_shards * rho);
-  for (int t = 0; t < p->n_dst_shards; ++t)
-    for (int j = 0; j < rho; ++j) rep[(size_t)t * rho + j] = p->replicas[t][j];
-  std::vector<uint32_t> civ;
-  if (chunk <= kMaxChunkTable) {
-    civ.resize(chunk);
-    for (size_t i = 0; i < n; ++i) {
-      const uint64_t end = i + 1 < n ? host[i + 1].first_chunk : chunk;
-      for (uint64_t c = host[i].first_chunk; c < end; ++c) civ[c] = (uint32_t)i;
-    }
-  }
+  for (size_t i = 0; i < n; ++i) chunk += (p->intervals[i].len + chunk_bytes - 1) / chunk_bytes;
+  const size_t n_civ = chunk <= kMaxChunkTable ? (size_t)chunk : 0;
   const size_t iv_bytes = n * sizeof(DevInterval);
-  const size_t rep_bytes = (rep.size() * sizeof(int32_t) + 15) & ~size_t(15);
-  const size_t bytes = iv_bytes + rep_bytes + civ.size() * sizeof(uint32_t);
-  void *mem = nullptr;
-  if (hipMalloc(&mem, bytes) != hipSuccess) return CCL_ERR_NOMEM;
-  // Synchronous copies: the host staging vectors die when this returns.
-  if (hipMemcpy(mem, host.data(), iv_bytes, hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy((char *)mem + iv_bytes, rep.data(), rep.size() * sizeof(int32_t),
-                hipMemcpyHostToDevice) != hipSuccess ||
-      (!civ.empty() && hipMemcpy((char *)mem + iv_bytes + rep_bytes, civ.data(),
-                                 civ.size() * sizeof(uint32_t), hipMemcpyHostToDevice) != hipSuccess)) {
-    (void)hipFree(mem);
-    return CCL_ERR_HIP;
-  }
+  const size_t n_rep = (size_t)p->n_dst_shards * rho;
+  const size_t rep_bytes = (n_rep * sizeof(int32_t) + 15) & ~size_t(15);
+  const size_t bytes = iv_bytes + rep_bytes + n_civ * sizeof(uint32_t);
   DevicePlanCache e;
   e.device = dev;
-  e.table = mem;
   e.rep_offset = iv_bytes;
-  e.chunk_iv_offset = civ.empty() ? 0 : iv_bytes + rep_bytes;
+  e.chunk_iv_offset = n_civ ? iv_bytes + rep_bytes : 0;
   e.chunk_bytes = chunk_bytes;
   e.total_chunks = chunk;
+  if (bytes == 0) {  // no intervals: nothing to upload
+    e.upload_done = true;
+    p->dev.push_back(e);
+    *out = e;
+    return CCL_OK;
+  }
+  if (hipHostMalloc(&e.staging, bytes, hipHostMallocDefault) != hipSuccess) return CCL_ERR_NOMEM;
+  char *h = (char *)e.staging;
+  DevInterval *hiv = (DevInterval *)h;
+  uint64_t first = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const PlanInterval &iv = p->intervals[i];
+    hiv[i] = DevInterval{iv.src_off, iv.dst_off, iv.len, first, iv.src_local, iv.dst_shard};
+    first += (iv.len + chunk_bytes - 1) / chunk_bytes;
+  }
+  int32_t *hrep = (int32_t *)(h + iv_bytes);
+  for (int t = 0; t < p->n_dst_shards; ++t)
+    for (int j = 0; j < rho; ++j) hrep[(size_t)t * rho + j] = p->replicas[t][j];
+  if (n_civ) {
+    uint32_t *hciv = (uint32_t *)(h + iv_bytes + rep_bytes);
+    for (size_t i = 0; i < n; ++i) {
+      const uint64_t end = i + 1 < n ? hiv[i + 1].first_chunk : chunk;
+      for (uint64_t c = hiv[i].first_chunk; c < end; ++c) hciv[c] = (uint32_t)i;
+    }
+  }
+  if (hipMalloc(&e.table, bytes) != hipSuccess) {
+    (void)hipHostFree(e.staging);
+    return CCL_ERR_NOMEM;
+  }
+  if (hipEventCreateWithFlags(&e.uploaded, hipEventDisableTiming) != hipSuccess ||
+      hipMemcpyAsync(e.table, e.staging, bytes, hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(e.uploaded, stream) != hipSuccess) {
+    // if the copy was enqueued (only the event record failed) it still
+    // reads the staging buffer and writes the table: drain it first
+    (void)hipStreamSynchronize(stream);
+    if (e.uploaded) (void)hipEventDestroy(e.uploaded);
+    (void)hipFree(e.table);
+    (void)hipHostFree(e.staging);
+    return CCL_ERR_HIP;
+  }
+  e.upload_stream = stream;
   p->dev.push_back(e);
   *out = e;
   return CCL_OK;
@@ -407,7 +440,7 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   const int cus = device_cu_count(dev);
   if (cus <= 0) return CCL_ERR_HIP;
   DevicePlanCache e;
-  ccl_status_t st = device_table(p, dev, l.chunk_bytes, &e);
+  ccl_status_t st = device_table(p, dev, l.chunk_bytes, stream, &e);
   if (st) return st;
   ReshardArgs a{};
   for (int i = 0; i < p->n_src; ++i) a.src[i] = (const char *)src[i];
@@ -453,7 +486,7 @@ ccl_status_t reshard_fp8_launch(ccl_plan *p, const void *const *src, void *const
   // chunks hold whole blocks
   const uint64_t chunk = std::max<uint64_t>(block_bytes, l.chunk_bytes / block_bytes * block_bytes);
   DevicePlanCache e;
-  ccl_status_t st = device_table(p, dev, chunk, &e);
+  ccl_status_t st = device_table(p, dev, chunk, stream, &e);
   if (st) return st;
   ReshardFp8Args a{};
   for (int i = 0; i < p->n_src; ++i) a.src[i] = (const char *)src[i];
@@ -486,7 +519,12 @@ void reshard_release(ccl_plan *p) {
     int cur = 0;
     (void)hipGetDevice(&cur);
     (void)hipSetDevice(e.device);
-    (void)hipFree(e.table);
+    if (e.uploaded) {
+      (void)hipEventSynchronize(e.uploaded);  // the staging copy is read until then
+      (void)hipEventDestroy(e.uploaded);
+    }
+    if (e.table) (void)hipFree(e.table);
+    if (e.staging) (void)hipHostFree(e.staging);
     (void)hipSetDevice(cur);
   }
   p->dev.clear();

@@ -355,11 +355,16 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
  *   dst_bufs   one pointer per destination-mesh rank, likewise.
  *   Any overlap of two destination buffers, or of a source and a
  *   destination buffer, gives CCL_ERR_ALIASING.
- * The first call for a device and chunk size allocates device memory for the
- * plan's interval table and copies it there synchronously (hipMalloc, then
- * blocking hipMemcpy); later calls reuse it until ccl_plan_destroy.  So make
- * that first call outside stream capture.  The same holds for
- * ccl_reshard_copy_fp8, whose chunks are rounded to whole 128-element blocks.
+ * The first call for a device and chunk size allocates the plan's device
+ * interval table and a pinned host copy of it (hipMalloc, hipHostMalloc), and
+ * uploads the table with an asynchronous copy on `stream`, ordered before the
+ * copy kernel; the host does not wait.  The plan keeps both allocations until
+ * ccl_plan_destroy.  A call on another stream while that upload may still be
+ * in flight makes its stream wait for it (an event wait, not a host wait).
+ * Because of the two allocations, make that first call outside stream
+ * capture; later calls allocate nothing and can be captured.  The same holds
+ * for ccl_reshard_copy_fp8, whose chunks are rounded to whole 128-element
+ * blocks.
  */
 ccl_status_t ccl_reshard_copy(const ccl_plan_t *plan, const void *const *src_bufs,
                               void *const *dst_bufs, void *stream,
@@ -392,7 +397,9 @@ ccl_status_t ccl_reshard_copy_fp8(const ccl_plan_t *plan, const void *const *src
                                   void *const *dst_codes, float *const *dst_scales, void *stream,
                                   const ccl_launch_config_t *cfg);
 
-/* Release a plan and its device table.  Work that uses it must be complete. */
+/* Release a plan, its device tables and their pinned host copies (waiting
+ * for a table upload still in flight).  Copy kernels that use the plan must
+ * be complete. */
 ccl_status_t ccl_plan_destroy(ccl_plan_t *plan);
 
 /* Inspection: interval count, one interval, local buffer bytes of a mesh rank

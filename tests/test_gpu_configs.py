@@ -13,6 +13,11 @@ Workloads (seed 0, numpy PCG64, rank r = r-th draw):
          sum/min/max, chunk 16 KiB .. 1 MiB                    -> full oracle up to
                                                                  16 MiB per rank,
                                                                  samples above
+  LDS    the same sweep's chunk axis through the LDS pipeline (2, 3 and 4
+         stages; 16 KiB, 128 KiB and 1 MiB chunks) on 64 MiB (+ a ragged
+         tail) and 256 MiB per rank, bf16 and fp32     -> bit-equal to the
+                                                          register-direct
+                                                          kernel + samples
 The 1 GiB points draw their inputs on the GPU (PyTorch's seeded generator) and
 copy back only the sampled inputs for the oracle.
 """
@@ -170,7 +175,7 @@ def test_ar_sweep_sizes(nbytes, dtype):
     P = 8
     esz = 4 if dtype == "f32" else 2
     n = nbytes // esz
-    ops = ["sum", "min", "max"] if nbytes <= 64 << 20 else ["sum"]
+    ops = ["sum", "min", "max"]
     if nbytes <= 16 << 20:
         xs = si.rank_buffers(P, n, dtype, "uniform", seed=0)
         dx = [up(x) for x in xs]
@@ -195,3 +200,55 @@ def test_ar_sweep_chunks(chunk, op):
     P, n = 8, (64 << 20) // 2 + 3  # 64 MiB bf16 per rank plus a ragged tail
     dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=1, device=DEV)
     _ar_sampled(dx, P, n, "bf16", op, cfg=ccl.LaunchConfig(chunk_bytes=chunk), k=50_000)
+
+
+_DEV_CACHE: dict = {}
+
+
+def _cached_inputs(P, n, dtype, seed):
+    """Device inputs drawn once per (P, n, dtype, seed) and reused by the
+    parametrizations that follow; only the latest set is kept."""
+    key = (P, n, dtype, seed)
+    if key not in _DEV_CACHE:
+        _DEV_CACHE.clear()
+        torch.cuda.empty_cache()
+        _DEV_CACHE[key] = si.device_rank_buffers(P, n, dtype, "uniform", seed=seed, device=DEV)
+    return _DEV_CACHE[key]
+
+
+# bytes per rank: 64 MiB plus a ragged tail (3 bf16 or 1 fp32 element), and 256 MiB
+LDS_SIZES = [(64 << 20) + 6, 256 << 20]
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4])
+@pytest.mark.parametrize("chunk", [16 << 10, 128 << 10, 1 << 20])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("nbytes", LDS_SIZES)
+def test_lds_pipeline_sweep_chunks(nbytes, dtype, chunk, stages):
+    """The LDS pipeline at the sweep's chunk sizes on large buffers: up to 256
+    tiles per chunk walk its tile cursor and vmcnt bookkeeping.  The outputs
+    must equal the register-direct kernel's bit for bit (same fold, same
+    order) and the oracle at sampled indices; every replica is identical."""
+    P = 8
+    esz = 4 if dtype == "f32" else 2
+    n = nbytes // esz
+    print(f"LDS sweep: {dtype} n={n} chunk={chunk} stages={stages}", flush=True)
+    dx = _cached_inputs(P, n, dtype, 3)
+    ops = ["sum", "min", "max"] if nbytes < (256 << 20) or chunk == (128 << 10) else ["sum"]
+    st = torch.cuda.current_stream()
+    for op in ops:
+        ref = [torch.empty_like(t) for t in dx]
+        ccl.check(ccl.ccl_all_reduce(dx, ref, P, n, ccl.DTYPES[dtype], ccl.OPS[op], st,
+                                     ccl.LaunchConfig(chunk_bytes=chunk, stages=1)))
+        outs = [torch.empty_like(t) for t in dx]
+        ccl.check(ccl.ccl_all_reduce(dx, outs, P, n, ccl.DTYPES[dtype], ccl.OPS[op], st,
+                                     ccl.LaunchConfig(chunk_bytes=chunk, stages=stages)))
+        torch.cuda.synchronize()
+        for q in range(P):
+            assert torch.equal(outs[q], ref[q]), (op, q)
+        idx = si.sample_indices(n, 50_000, seed=stages)
+        xin = gather_at(dx, idx, dtype)
+        want = oracle.fold_at(xin, dtype, op, np.arange(idx.size, dtype=np.uint64))
+        got = gather_at([outs[P - 1]], idx, dtype)[0]
+        assert_parity(got, want, dtype, op, f"LDS S={stages} chunk={chunk} {dtype} {op}")
+        del ref, outs

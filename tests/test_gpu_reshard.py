@@ -471,3 +471,51 @@ def test_reshard_fp8_weight_full_size_sampled():
         it = torch.from_numpy(idx).to(DEV)
         np.testing.assert_array_equal(codes[l][it].cpu().numpy(), wc)
         np.testing.assert_array_equal(scales[l][torch.from_numpy(blocks).to(DEV)].cpu().numpy(), wf)
+
+
+def test_first_copy_is_stream_ordered_behind_queued_work():
+    """A fresh plan's first copy uploads its interval table with an
+    asynchronous copy on the caller's stream: issued behind ~26 ms of queued
+    all-reduces on a side stream it returns while that stream is still busy,
+    and its results equal the oracle.  A copy of the same plan issued at once
+    on a second stream waits (on the GPU) for that upload; so does the FP8
+    variant's first call, which builds its own table."""
+    shape = (512, 1024)
+    src = ([1, 4], 0, ["R", ("S", 0)])
+    dst = ([2, 2], 4, ["R", ("S", 0)])
+    G = si.tensor(shape, "bf16", "w002", seed=77)
+    src_bufs = local_blocks(G, src)
+    want = oracle.reshard(shape, src, dst, src_bufs)
+    want8 = oracle.reshard_fp8(shape, src, dst, src_bufs, "bf16")
+    dsrc = [torch.from_numpy(np.ascontiguousarray(b).view(np.uint8).copy()).to(DEV)
+            for b in src_bufs]
+    nd = want[0].nbytes
+    ddst = [[torch.full((nd,), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(4)]
+            for _ in range(2)]
+    codes = [torch.full((nd // 2,), 0xEE, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    scales = [torch.zeros(nd // 2 // 128, dtype=torch.float32, device=DEV) for _ in range(4)]
+    Pb, nb = 8, 128 << 20  # 8 x 256 MiB bf16: one all-reduce is ~0.65 ms
+    bx = [torch.zeros(nb, dtype=torch.int16, device=DEV) for _ in range(Pb)]
+    by = [torch.empty_like(t) for t in bx]
+    torch.cuda.synchronize()
+    plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
+    side, other = torch.cuda.Stream(), torch.cuda.Stream()
+    try:
+        for _ in range(40):  # few long launches: ~26 ms of queued work
+            ccl.check(ccl.ccl_all_reduce(bx, by, Pb, nb, ccl.CCL_BFLOAT16, ccl.CCL_SUM, side))
+        ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst[0], side), "first copy")
+        ccl.check(ccl.ccl_reshard_copy_fp8(plan, dsrc, codes, scales, side), "first fp8 copy")
+        assert not side.query(), "the first copies waited for the side stream"
+        ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst[1], other), "copy on another stream")
+        other.synchronize()
+        side.synchronize()
+        for k in range(2):
+            for l in range(4):
+                np.testing.assert_array_equal(ddst[k][l].cpu().numpy().view(np.uint16), want[l])
+        for l in range(4):
+            np.testing.assert_array_equal(codes[l].cpu().numpy(), want8[l][0])
+            np.testing.assert_array_equal(scales[l].cpu().numpy().view(np.uint32),
+                                          want8[l][1].view(np.uint32))
+    finally:
+        torch.cuda.synchronize()
+        ccl.check(ccl.ccl_plan_destroy(plan))

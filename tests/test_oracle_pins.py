@@ -302,11 +302,9 @@ def _tiny_layouts(ndim, shape):
 def test_reshard_all_tiny_layouts_against_torch_chunk(shape):
     G = global_iota(shape)
     layouts = list(_tiny_layouts(len(shape), shape))
-    rng = np.random.default_rng(len(shape))
-    pairs = [(a, b) for a in layouts for b in layouts]
-    sel = rng.choice(len(pairs), size=min(300, len(pairs)), replace=False)
-    for i in sel:
-        (sd, spl), (dd, dpl) = pairs[i]
+    # every ordered pair of layouts: meshes of 1-6 ranks, any placement with at
+    # most one sharded axis
+    for (sd, spl), (dd, dpl) in itertools.product(layouts, layouts):
         src = (sd, 0, spl)
         dst = (dd, int(np.prod(sd)) + 1, dpl)
         src_bufs = local_blocks(G, src)
@@ -565,3 +563,120 @@ def test_quantization_scale_that_underflows_is_one():
     assert 0 < s < 2.0 ** -126 and s == np.float32(amax) / np.float32(448)
     assert amax / np.float64(s) > 448           # the quotient overshoots 448 ...
     assert codes[0] == 0x7E and codes[1] == 0xFE  # ... and saturates
+
+
+def _e4m3_codes_from_quotients(q: np.ndarray) -> np.ndarray:
+    """fp32 quotients -> E4M3 codes: saturate at +-448, then PyTorch's
+    round-to-nearest-even conversion (which has no saturation of its own)."""
+    t = torch.from_numpy(np.ascontiguousarray(q, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _blockwise_reference(xf: np.ndarray, block: int = 128):
+    """The format written out with numpy and PyTorch only: per block an fp32
+    amax, scale = amax / 448 in fp32 (1 when that is zero), code = E4M3 of the
+    fp32 quotient x / scale."""
+    nb = (xf.size + block - 1) // block
+    scales = np.empty(nb, np.float32)
+    q = np.empty(xf.size, np.float32)
+    for b in range(nb):
+        sl = slice(b * block, min((b + 1) * block, xf.size))
+        amax = np.max(np.abs(xf[sl])).astype(np.float32)
+        s = np.float32(amax / np.float32(448.0))
+        s = np.float32(1.0) if s == 0 else s
+        scales[b] = s
+        q[sl] = xf[sl] / s
+    return _e4m3_codes_from_quotients(q), scales
+
+
+def _discriminating_blocks(rng, n_scales: int = 2000, keep: int = 64) -> np.ndarray:
+    """128-element fp32 blocks, one per scale, each holding its amax and
+    elements whose quotient x / scale lies within an fp32 ulp of a midpoint
+    between two E4M3 values, kept only where the code of x / scale differs
+    from the code of x * (1 / scale)."""
+    amax = (rng.uniform(1, 2, n_scales) * np.exp2(rng.integers(-20, 20, n_scales))).astype(np.float32)
+    s = (amax / np.float32(448.0)).astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    vals = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    vals = np.unique(vals[vals > 0])
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = (mids[rng.integers(0, mids.size, n_scales)] * s).astype(np.float32)
+    cands = [np.nextafter(x, np.float32(-np.inf), dtype=np.float32), x,
+             np.nextafter(x, np.float32(np.inf), dtype=np.float32)]
+    blocks = []
+    for i in range(n_scales):
+        good = [c[i] for c in cands
+                if _e4m3_codes_from_quotients(np.array([c[i] / s[i]]))[0]
+                != _e4m3_codes_from_quotients(np.array([c[i] * inv[i]]))[0]]
+        if not good:
+            continue
+        y = (rng.uniform(-1, 1, 128) * amax[i]).astype(np.float32)
+        y[0] = amax[i]
+        for j, g in enumerate(good):
+            y[1 + 2 * j], y[2 + 2 * j] = g, -g
+        blocks.append(y)
+        if len(blocks) == keep:
+            break
+    return np.concatenate(blocks)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_blockwise_quantization_equals_numpy_torch_chain(dtype):
+    """orc_quantize_e4m3 bit for bit against the format rebuilt outside the
+    oracle (numpy fp32 amax and division, PyTorch's E4M3 conversion), on
+    ordinary blocks, an all-zero block, a block whose quotient underflows, a
+    block with amax above 448 and a ragged last block."""
+    rng = np.random.default_rng(41)
+    n = 128 * 24 + 37
+    if dtype == "f32":
+        x = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 30, n))).astype(np.float32)
+        x[128:256] = 0.0
+        x[256:384] = np.float32(2.0 ** -149) * rng.choice([-1, 0, 1], 128)
+        x[384:512] = rng.uniform(-3000, 3000, 128).astype(np.float32)
+        xs = x
+    elif dtype == "bf16":
+        x = si.rank_buffers(1, n, "bf16", "w002", seed=5)[0].copy()
+        x[128:256] = 0
+        big = si.to_bf16_bits(rng.uniform(-3000, 3000, 128).astype(np.float32))
+        x[384:512] = big
+        xs = x
+    else:
+        xf = (rng.standard_normal(n) * 10).astype(np.float16)
+        xf[128:256] = 0
+        xf[384:512] = rng.uniform(-60000, 60000, 128).astype(np.float16)
+        xs = xf.view(np.uint16)
+    codes, scales = oracle.quantize_e4m3(xs, dtype)
+    if dtype == "f32":
+        xf32 = xs
+    elif dtype == "bf16":
+        xf32 = si.bf16_bits_to_f32(xs)
+    else:
+        xf32 = xs.view(np.float16).astype(np.float32)
+    want_codes, want_scales = _blockwise_reference(xf32)
+    np.testing.assert_array_equal(scales.view(np.uint32), want_scales.view(np.uint32))
+    np.testing.assert_array_equal(codes, want_codes)
+
+
+def test_blockwise_quantization_chain_catches_reciprocal_and_early_clamp():
+    """Blocks built on E4M3 rounding midpoints: the oracle matches the division
+    x / scale there, while the two plausible slips -- multiplying by the fp32
+    reciprocal, or clamping x (rather than the quotient) to +-448 -- give other
+    codes on the same inputs, so the pin above would catch either."""
+    rng = np.random.default_rng(43)
+    x = _discriminating_blocks(rng)
+    assert x.size == 64 * 128
+    codes, scales = oracle.quantize_e4m3(x, "f32")
+    want_codes, want_scales = _blockwise_reference(x)
+    np.testing.assert_array_equal(scales.view(np.uint32), want_scales.view(np.uint32))
+    np.testing.assert_array_equal(codes, want_codes)
+    s = np.repeat(want_scales, 128)[: x.size]
+    recip = _e4m3_codes_from_quotients(x * (np.float32(1.0) / s))
+    assert np.count_nonzero(recip != codes) >= 64
+    # clamping before the division: blocks whose amax exceeds 448
+    big = (rng.uniform(-1, 1, 128 * 4) * 3000).astype(np.float32)
+    codes_b, scales_b = oracle.quantize_e4m3(big, "f32")
+    want_b, _ = _blockwise_reference(big)
+    np.testing.assert_array_equal(codes_b, want_b)
+    sb = np.repeat(scales_b, 128)
+    early = _e4m3_codes_from_quotients(np.clip(big, -448.0, 448.0).astype(np.float32) / sb)
+    assert np.count_nonzero(early != codes_b) >= 128
