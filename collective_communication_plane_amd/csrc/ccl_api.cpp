@@ -272,13 +272,50 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
   // up to 16 KiB: one workgroup per row, at most 3 per CU for rows of 4-8 KiB,
   // shorter and longer ones uncapped.
   const uint64_t row_bytes = hidden * sz;
+  // chunk_bytes below the row length asks for the split-row kernels, whose
+  // pieces are one vector per lane: 4 KiB per rank.  By default rows longer
+  // than 8 KiB per rank take them at P >= 6 (bf16, 2 GiB of input: +9-10 %
+  // at P = 8 on 16 KiB rows, +4-7 % on 32 KiB rows, +3-4 % at P = 6, +16 %
+  // at P = 12; they cost 1/P of the traffic extra, which loses at P <= 4, and
+  // break even on 8 KiB rows).
+  const uint64_t max_pieces = uint64_t(1) << 31;
+  bool split = false;
+  if (l.chunk_set && l.chunk_bytes < row_bytes) {
+    if (l.chunk_bytes != ccl::kSplitPieceBytes || (l.stages_set && l.stages != 1))
+      return CCL_ERR_UNSUPPORTED;
+    if (rows * ccl::rms_split_pieces(row_bytes) > max_pieces) return CCL_ERR_UNSUPPORTED;
+    split = true;
+  } else if (!l.chunk_set && !l.stages_set && nranks >= 6 && row_bytes > 8192 &&
+             rows * ccl::rms_split_pieces(row_bytes) <= max_pieces) {
+    split = true;
+  }
+  // Their norm pass writes through past 256 MiB per rank, where every output
+  // row starts on a 256-byte line (P = 8, 384 MiB per rank: +4-17 % over
+  // nontemporal stores; at 256 MiB per rank the two are equal).
+  if (split && !l.store_pol_set && rows * row_bytes > (uint64_t(256) << 20) &&
+      row_bytes % 256 == 0) {
+    bool lines = true;
+    for (int q = 0; q < nranks; ++q) lines = lines && (uintptr_t)recv[q] % 256 == 0;
+    l.store_wt = lines;
+  } else if (split && !l.store_pol_set) {
+    l.store_wt = false;
+  }
+  if (split) l.store_pol_set = true;
   if (!l.stages_set) l.stages = row_bytes > 16384 ? 2 : 1;
   if (!l.occupancy_set) {
-    if (l.stages == 2) l.occupancy = 1;
-    else l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+    if (split) {
+      l.occupancy = 4;   // fold pass
+      l.occupancy2 = 2;  // norm pass
+    } else if (l.stages == 2) {
+      l.occupancy = 1;
+    } else {
+      l.occupancy = (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+    }
+  } else {
+    l.occupancy2 = l.occupancy;
   }
   ccl::RmsDesc d{nranks, dtype, rows, hidden, eps, send, recv, gamma};
-  return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream);
+  return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream, split);
 }
 
 ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t count, int dtype,

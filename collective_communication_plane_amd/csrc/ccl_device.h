@@ -62,6 +62,17 @@ __device__ __forceinline__ void st_wt_b32(char *base, uint64_t off, uint32_t v) 
   __builtin_amdgcn_raw_buffer_store_b32(v, wt_rsrc(base), (int)off, 0, kPolNtSc1);
 }
 
+// A 16-byte load through a raw buffer resource over [base, base + bytes):
+// `base` must be the same in every lane, `off` is the lane's byte offset.  A
+// load outside the range (bytes = 0 makes every load so) returns zero and
+// reads nothing.  NT: the nontemporal cache-policy bit.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_row(const char *base, uint32_t bytes, int off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)bytes, kRawBufferWord3);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0));
+}
+
 // A pointer the caller knows to be the same in every lane, moved to scalar
 // registers so that a buffer resource can be built from it without a loop
 // over lanes.

@@ -75,6 +75,7 @@ struct Launch {
   bool nt_load;
   bool nt_store;
   int occupancy;   // max resident workgroups per CU, 0 = no cap
+  int occupancy2 = 0;  // the split-row RMSNorm's second (norm) pass
   bool chunk_set = false;      // chunk_bytes came from the caller
   bool stages_set = false;     // stages came from the caller
   bool occupancy_set = false;  // occupancy came from the caller
@@ -128,7 +129,22 @@ struct RmsDesc {
   const void *gamma;
 };
 constexpr int kRmsMaxRowVecs = 8 * kThreads;  // 16-byte vectors per row
-ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t stream);
+// Split-row form: rows cut into pieces of one vector per lane (4 KiB per
+// rank), a fold pass and a norm pass with one workgroup per piece each; the
+// passes hand over one fp32 partial sum of squares per piece through device
+// scratch.
+constexpr uint64_t kSplitPieceBytes = (uint64_t)kThreads * kVecBytes;
+inline uint64_t rms_split_pieces(uint64_t row_bytes) {
+  return (row_bytes + kSplitPieceBytes - 1) / kSplitPieceBytes;
+}
+inline uint64_t rms_split_scratch_bytes(uint64_t rows, uint64_t row_bytes) {
+  return rows * rms_split_pieces(row_bytes) * sizeof(float);
+}
+// split: run the split-row kernel.  Its scratch is `scratch` when given (at
+// least rms_split_scratch_bytes), else the calling stream's own buffer, which
+// the library allocates on first use and keeps.
+ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t stream, bool split,
+                               void *scratch = nullptr);
 
 // ------------------------------------------------------------------ reshard
 

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "ccl_device.h"
 #include "ccl_internal.h"
@@ -234,6 +236,131 @@ __global__ void __launch_bounds__(kThreads) ar_rmsnorm_pipe_kernel(RmsArgs a) {
   }
 }
 
+// ------------------------------------------------------------ split rows
+//
+// The same result from two kernels whose workgroups each own one piece of a
+// row: 256 vectors, i.e. 4 KiB per rank, the plain all-reduce's unit, and a
+// short-lived workgroup per piece.  A workgroup that owns a whole row walks
+// 4 x 4 KiB per rank at P = 8 and runs ~15 % below the all-reduce; pieces
+// of one row cannot wait for each other inside a kernel without giving most
+// of that back (measured: pieces publishing partial sums to each other and
+// polling ran at 4.5-4.9 TB/s against 5.8-6.3 for the same kernel without
+// the wait), so the norm waits for a kernel boundary instead:
+//   fold pass  folds the piece's P inputs in fp32 in rank order, rounds to
+//              the element type (the reduce-scatter value s), parks s in
+//              recv[0] at its own position, and writes the piece's sum of
+//              squares (lanes, then a wave butterfly, then the four waves in
+//              order) to part[row * K + piece];
+//   norm pass  reads the row's K partial sums and adds them in piece order,
+//              reads s back from recv[0] and gamma, and stores
+//              s * inv * gamma to all P outputs, recv[0] included.
+// Each position is read and then written by the same lane of the same piece
+// in both passes, so the call may still run in place (recv[q] == send[r]).
+// The cost over the one-pass kernels is one extra write and read of s
+// (hidden * size bytes per row, 1/P of the input).
+constexpr int kSplitPieceVecs = kThreads;  // one vector per lane
+
+template <int DT, int PMAX, bool NTL>
+__global__ void __launch_bounds__(kThreads) ar_rmsnorm_fold_kernel(RmsArgs a, float *part, int K) {
+  constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
+  constexpr int V = kVecBytes / esz;
+  __shared__ float wave_part[kThreads / 64];
+  const int P = a.P;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t row = blockIdx.x / (unsigned)K;
+  const int piece = (int)(blockIdx.x - row * (unsigned)K);
+  const uint32_t v = (uint32_t)piece * kSplitPieceVecs + threadIdx.x;
+  const bool live = v < a.row_vecs;
+  // lanes past the end of a short last piece re-read the row's last vector
+  // (so every load is unconditional) and store nothing
+  const uint32_t vc = live ? v : a.row_vecs - 1;
+  const uint64_t row_base = row * (uint64_t)a.hidden * esz;
+
+  // Every rank's load is issued before the first is used.  They go through
+  // buffer resources over this row; ranks r >= P get an empty range, whose
+  // loads return zero without touching memory, so no load sits behind a
+  // per-rank branch (with branches the compiler copied one rank's result into
+  // a register it had reserved and waited for the first loads there).  That
+  // zero is turned into -0.0 by a uniform mask, and x + (-0.0) == x for every
+  // x, -0.0 included, so folding all PMAX slots gives the P-rank fold bit for
+  // bit without a per-rank branch in the fold either.
+  constexpr uint32_t kNegZero = DT == CCL_FLOAT32 ? 0x80000000u : 0x80008000u;
+  u32x4 x[PMAX];
+#pragma unroll
+  for (int r = 0; r < PMAX; ++r) {
+    x[r] = ld_row<NTL>(a.in[r] + row_base, r < P ? a.row_vecs * kVecBytes : 0u,
+                       (int)(vc * kVecBytes));
+    x[r] ^= (r < P ? 0u : kNegZero);
+  }
+  const u32x4 sv = fold_vec<DT, CCL_SUM, PMAX>(x, PMAX);
+  float f[8];
+  widen_vec<DT>(sv, f);
+  float ss = 0.f;
+  if (live) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) ss += f[e] * f[e];
+    st_plain(a.out[0] + row_base + (uint64_t)v * kVecBytes, sv);
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) wave_part[wave] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) t += wave_part[w];
+    part[row * (unsigned)K + piece] = t;
+  }
+}
+
+template <int DT, int PMAX, int SP>
+__global__ void __launch_bounds__(kThreads) ar_rmsnorm_norm_kernel(RmsArgs a, const float *part,
+                                                                    int K) {
+  constexpr int esz = DT == CCL_FLOAT32 ? 4 : 2;
+  constexpr int V = kVecBytes / esz;
+  const int P = a.P;
+  const uint64_t row = blockIdx.x / (unsigned)K;
+  const int piece = (int)(blockIdx.x - row * (unsigned)K);
+  const uint32_t v = (uint32_t)piece * kSplitPieceVecs + threadIdx.x;
+  const bool live = v < a.row_vecs;
+  const uint32_t vc = live ? v : a.row_vecs - 1;
+  const uint64_t row_base = row * (uint64_t)a.hidden * esz;
+  const u32x4 gv = ld_plain(a.gamma + (uint64_t)vc * kVecBytes);
+  const u32x4 sv = ld_plain(a.out[0] + row_base + (uint64_t)vc * kVecBytes);
+  float total = 0.f;
+  for (int j = 0; j < K; ++j) total += part[row * (unsigned)K + j];
+  const float inv = 1.0f / sqrtf(total / (float)a.hidden + a.eps);
+  if (live) {
+    float g[8], f[8], y[8];
+    widen_vec<DT>(gv, g);
+    widen_vec<DT>(sv, f);
+#pragma unroll
+    for (int e = 0; e < V; ++e) y[e] = (f[e] * inv) * g[e];
+    const u32x4 o = narrow_vec<DT>(y);
+    const uint64_t obase = row_base + (uint64_t)piece * kSplitPieceVecs * kVecBytes;
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q)
+      if (q < P) st_pol<SP>(a.out[q] + obase, (uint64_t)threadIdx.x * kVecBytes, o);
+  }
+}
+
+template <int DT, int PMAX, bool NTL, int SP>
+void launch_split_pm(const RmsArgs &a, float *part, int K, unsigned grid, size_t lds_fold,
+                     size_t lds_norm, hipStream_t st) {
+  hipLaunchKernelGGL((ar_rmsnorm_fold_kernel<DT, PMAX, NTL>), dim3(grid), dim3(kThreads), lds_fold,
+                     st, a, part, K);
+  hipLaunchKernelGGL((ar_rmsnorm_norm_kernel<DT, PMAX, SP>), dim3(grid), dim3(kThreads), lds_norm,
+                     st, a, (const float *)part, K);
+}
+
+template <int DT, bool NTL, int SP>
+hipError_t launch_split_p(const RmsArgs &a, float *part, int K, unsigned grid, size_t lds_fold,
+                          size_t lds_norm, hipStream_t st) {
+  if (a.P <= 4) launch_split_pm<DT, 4, NTL, SP>(a, part, K, grid, lds_fold, lds_norm, st);
+  else if (a.P <= 8) launch_split_pm<DT, 8, NTL, SP>(a, part, K, grid, lds_fold, lds_norm, st);
+  else launch_split_pm<DT, 16, NTL, SP>(a, part, K, grid, lds_fold, lds_norm, st);
+  return hipGetLastError();
+}
+
 template <int DT, bool NTL, int SP>
 hipError_t launch_p(const RmsArgs &a, bool pipe, unsigned grid, size_t lds, hipStream_t st) {
   if (pipe) {
@@ -265,9 +392,71 @@ hipError_t launch_nt(const RmsArgs &a, const Launch &l, bool pipe, unsigned grid
   return launch_p<DT, false, ST_PLAIN>(a, pipe, grid, lds, st);
 }
 
+template <int DT>
+hipError_t launch_split_nt(const RmsArgs &a, const Launch &l, float *part, int K, unsigned grid,
+                           size_t lds_fold, size_t lds_norm, hipStream_t st) {
+  const int sp = !l.nt_store ? ST_PLAIN : (l.store_pol_set && l.store_wt) ? ST_WT : ST_NT;
+  if (l.nt_load) {
+    if (sp == ST_WT) return launch_split_p<DT, true, ST_WT>(a, part, K, grid, lds_fold, lds_norm, st);
+    if (sp == ST_NT) return launch_split_p<DT, true, ST_NT>(a, part, K, grid, lds_fold, lds_norm, st);
+    return launch_split_p<DT, true, ST_PLAIN>(a, part, K, grid, lds_fold, lds_norm, st);
+  }
+  if (sp == ST_WT) return launch_split_p<DT, false, ST_WT>(a, part, K, grid, lds_fold, lds_norm, st);
+  if (sp == ST_NT) return launch_split_p<DT, false, ST_NT>(a, part, K, grid, lds_fold, lds_norm, st);
+  return launch_split_p<DT, false, ST_PLAIN>(a, part, K, grid, lds_fold, lds_norm, st);
+}
+
+// Partial sums of the split-row kernels, one buffer per (device, stream):
+// calls on one stream are ordered, so they can share it; calls on different
+// streams may overlap, so they must not.  Allocated on first use; a call
+// that needs more allocates a larger buffer (at least twice the old one) and
+// keeps the old one too, since queued kernels or a captured graph may still
+// use it.  Every buffer lives until the process ends.  Every slot a call
+// reads was written by the same call's fold pass, so nothing needs clearing.
+// A stream in capture cannot allocate: *out is then null when the stream has
+// no buffer large enough, and the caller runs a one-pass kernel instead.
+struct StreamScratch {
+  int device;
+  hipStream_t stream;
+  void *mem;
+  size_t bytes;
+};
+std::mutex g_scratch_mu;
+std::vector<StreamScratch> g_scratch;
+
+ccl_status_t stream_scratch(int dev, hipStream_t st, size_t need, void **out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  StreamScratch *e = nullptr;
+  for (auto &x : g_scratch)
+    if (x.device == dev && x.stream == st) e = &x;
+  if (e && e->bytes >= need) {
+    *out = e->mem;
+    return CCL_OK;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess) return CCL_ERR_HIP;
+  if (cap != hipStreamCaptureStatusNone) {
+    *out = nullptr;
+    return CCL_OK;
+  }
+  const size_t bytes = std::max<size_t>({need, size_t(1) << 20, e ? 2 * e->bytes : 0});
+  void *mem = nullptr;
+  if (hipMalloc(&mem, bytes) != hipSuccess) return CCL_ERR_NOMEM;
+  if (e) {
+    e->mem = mem;  // the old buffer stays allocated (see above)
+    e->bytes = bytes;
+  } else {
+    g_scratch.push_back(StreamScratch{dev, st, mem, bytes});
+  }
+  *out = mem;
+  return CCL_OK;
+}
+
 }  // namespace
 
-ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t stream) {
+ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l_in, hipStream_t stream,
+                               bool split, void *scratch) {
+  Launch l = l_in;
   RmsArgs a{};
   const int esz = dtype_size(d.dtype);
   for (int r = 0; r < d.P; ++r) {
@@ -280,6 +469,38 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   a.row_vecs = (uint32_t)(d.hidden * esz / kVecBytes);
   a.eps = d.eps;
   a.P = d.P;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
+  const uint64_t row_bytes = (uint64_t)a.row_vecs * kVecBytes;
+  void *part = scratch;
+  if (split && !part) {
+    ccl_status_t st = stream_scratch(dev, stream, rms_split_scratch_bytes(d.rows, row_bytes), &part);
+    if (st) return st;
+    if (!part) {
+      // in capture without scratch: the one-pass form this row length takes
+      // by default (the same result within the documented bound, other bits)
+      split = false;
+      l.stages = row_bytes > 16384 ? 2 : 1;
+      l.occupancy = l.stages == 2 ? 1 : (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+      l.store_wt = false;
+    }
+  }
+  if (split) {
+    // one workgroup per piece in each pass; grid = rows x pieces (checked to
+    // fit by the caller)
+    const int K = (int)rms_split_pieces(row_bytes);
+    const unsigned grid = (unsigned)(d.rows * (uint64_t)K);
+    const size_t lds_fold = occupancy_lds(l.occupancy, 64);
+    const size_t lds_norm = occupancy_lds(l.occupancy2, 0);
+    float *pf = (float *)part;
+    hipError_t err;
+    switch (d.dtype) {
+      case CCL_FLOAT32: err = launch_split_nt<CCL_FLOAT32>(a, l, pf, K, grid, lds_fold, lds_norm, stream); break;
+      case CCL_BFLOAT16: err = launch_split_nt<CCL_BFLOAT16>(a, l, pf, K, grid, lds_fold, lds_norm, stream); break;
+      default: err = launch_split_nt<CCL_FLOAT16>(a, l, pf, K, grid, lds_fold, lds_norm, stream); break;
+    }
+    return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
+  }
   // stages = 2: the row-pipelined kernel on a persistent grid of (residency
   // cap, else 1) workgroups per CU; stages = 1: one workgroup per row.
   const bool pipe = l.stages == 2;
@@ -287,8 +508,6 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t st
   if (l.workgroups) {
     grid = (uint64_t)l.workgroups;
   } else if (pipe) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
     const int cus = device_cu_count(dev);
     if (cus <= 0) return CCL_ERR_HIP;
     grid = (uint64_t)cus * (uint64_t)(l.occupancy > 0 ? l.occupancy : 1);

@@ -99,14 +99,20 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   nontemporal stores only
  *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
- *   all-reduce + RMSNorm  rows of up to 16 KiB per rank: one workgroup per
- *                   row; <= 3 WGs per CU for rows of 4-8 KiB, otherwise
- *                   residency bounded only by registers and the row buffer it
- *                   keeps in LDS.  Longer rows: the row-pipelined kernel
- *                   (stages = 2) on a persistent grid of one workgroup per CU.
- *                   It reads workgroups, stages (1 or 2; 3 and 4 give
- *                   CCL_ERR_UNSUPPORTED), nontemporal and occupancy and
- *                   ignores the rest
+ *   all-reduce + RMSNorm  P >= 6 with rows longer than 8 KiB per rank: the
+ *                   split-row form (chunk_bytes = 4096 below): a fold pass
+ *                   with <= 4 WGs per CU and a norm pass with <= 2, whose
+ *                   stores write through past 256 MiB per rank when every
+ *                   output and row starts on 256 bytes.  Otherwise rows of
+ *                   up to 16 KiB per rank: one workgroup per row; <= 3 WGs
+ *                   per CU for rows of 4-8 KiB, otherwise residency bounded
+ *                   only by registers and the row buffer it keeps in LDS.
+ *                   Longer rows: the row-pipelined kernel (stages = 2) on a
+ *                   persistent grid of one workgroup per CU.  It reads
+ *                   chunk_bytes (4096 or at least the row), workgroups,
+ *                   stages (1 or 2; 3 and 4 give CCL_ERR_UNSUPPORTED),
+ *                   nontemporal, occupancy (both passes of the split form)
+ *                   and store_policy and ignores the rest
  * Buffers whose inputs sit at a different offset mod 16 from their outputs
  * use a register-direct kernel that realigns the inputs in VGPRs; unless the
  * caller sets them, it runs 4 KiB chunks with <= 8 WGs per CU (reduce-scatter
@@ -129,6 +135,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                `stages` LDS buffers with asynchronous global->LDS loads,
  *                consumer waves fold and store them (clamped so the ring
  *                fits in 128 KiB).  The reshard copy is register-direct only.
+ *                For the fused RMSNorm: chunk_bytes = 4096 with rows longer
+ *                than that selects the split-row form (one workgroup per
+ *                4 KiB piece of a row in each of two passes); any other
+ *                value below the row length gives CCL_ERR_UNSUPPORTED.
  *                For the fused RMSNorm: 1 = one row at a time per workgroup,
  *                2 = two rows software-pipelined (the next row's inputs are
  *                loaded and folded while the current row is stored).
@@ -232,10 +242,24 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
  *   inv   = 1 / sqrt(mean over h of s[h]^2 + eps), computed in fp32;
  *   recv[q][t][h] = dtype(s[h] * inv * gamma[h]) for every q.
  * This equals reduce-scatter, RMSNorm on each owner's rows, then all-gather,
- * whenever each shard holds whole rows; here a workgroup owns whole rows, so
- * no shard boundary is needed.  The sum of squares is accumulated in fp32 in
- * a fixed order, so results are reproducible; against an exact norm the
- * relative error is at most about (hidden/2 + 4) * 2^-24.
+ * whenever each shard holds whole rows.  The sum of squares is accumulated in
+ * fp32 in a fixed order for a given launch form (the split-row form adds
+ * per-piece sums in piece order, the one-pass forms per-lane sums across the
+ * row), so results are reproducible; against an exact norm the relative error
+ * is at most about (hidden/2 + 4) * 2^-24 either way.
+ * The split-row form (see ccl_launch_config_t) runs two kernels: the first
+ * parks each row's folded values s in recv[0] (so recv[0] holds s, not the
+ * result, until the second kernel has run) and writes one fp32 partial sum
+ * per 4 KiB piece to scratch; the second scales and stores.  That scratch is
+ * the calling stream's own device buffer, 4 bytes per piece: the first such
+ * call on a (device, stream) allocates it with hipMalloc, a later call that
+ * needs more allocates a larger one (at least twice the size), and every such
+ * buffer is kept until the process ends.  A call made while its stream is
+ * being captured cannot allocate: if the stream has no buffer large enough
+ * yet, it runs the one-pass form instead (so make one eager call on the
+ * capturing stream first to capture the split form).  A captured call keeps
+ * the buffer of the stream it was captured on: replaying the graph while
+ * other calls run on that stream, or on two streams at once, races.
  *
  *   dtype  CCL_FLOAT32, CCL_BFLOAT16 or CCL_FLOAT16 (op is sum).
  *   gamma  hidden elements of dtype, device memory, 16-byte aligned.

@@ -51,7 +51,7 @@ def _check_replays(calls, inputs, outputs, replays=3):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):  # capture on the warmed-up stream
         calls(torch.cuda.current_stream())
     torch.cuda.synchronize()
     for k in range(replays):
@@ -125,8 +125,8 @@ def test_fused_and_reshard_calls_in_a_graph():
 
 def test_write_through_calls_in_a_graph():
     """Write-through stores (buffer stores with the device-scope bit) replay
-    bit-identically from a graph: the all-gather on line-aligned shards and
-    the row-pipelined RMSNorm by default, the all-reduce, reshard copy and FP8
+    bit-identically from a graph: the all-gather on line-aligned shards by
+    default, the split-row RMSNorm, the all-reduce, reshard copy and FP8
     codes by request."""
     P, n, m = 8, 65536, 8192
     wt = ccl.LaunchConfig(store_policy=1)
@@ -152,7 +152,7 @@ def test_write_through_calls_in_a_graph():
             ccl.check(ccl.ccl_all_reduce(x_ar, y_ar, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream, wt))
             ccl.check(ccl.ccl_all_gather(x_ag, y_ag, P, m, ccl.CCL_FLOAT32, stream))
             ccl.check(ccl.ccl_all_reduce_rmsnorm(x_n, y_n, P, rows, hidden, gamma, 1e-6,
-                                                 ccl.CCL_BFLOAT16, stream))
+                                                 ccl.CCL_BFLOAT16, stream, wt))
             ccl.check(ccl.ccl_reshard_copy(plan, src, dst, stream, wt))
             ccl.check(ccl.ccl_reshard_copy_fp8(plan, src, codes, scales, stream, wt))
 
@@ -161,3 +161,41 @@ def test_write_through_calls_in_a_graph():
     finally:
         torch.cuda.synchronize()
         ccl.check(ccl.ccl_plan_destroy(plan))
+
+
+def test_split_rmsnorm_in_a_graph_and_capture_fallback():
+    """The split-row RMSNorm (P = 8, 16 KiB rows: the default form) replays
+    bit-identically when captured on a stream that made an eager call first.
+    Captured on a fresh stream, which has no partial-sum scratch yet and
+    cannot allocate during capture, the call runs the one-pass form instead:
+    the replay equals an eager call with stages = 1."""
+    P, rows, hidden = 8, 40, 8192
+    x = [torch.empty(rows * hidden, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    y = [torch.empty_like(t) for t in x]
+    gamma = torch.empty(hidden, dtype=torch.bfloat16, device=DEV)
+
+    def calls(stream):
+        ccl.check(ccl.ccl_all_reduce_rmsnorm(x, y, P, rows, hidden, gamma, 1e-6,
+                                             ccl.CCL_BFLOAT16, stream))
+
+    _check_replays(calls, x + [gamma], y)
+
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(5)
+    _refill(x + [gamma], gen)
+    fresh = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=fresh):
+        calls(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    for o in y:
+        o.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    got = [o.clone() for o in y]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm(x, y, P, rows, hidden, gamma, 1e-6, ccl.CCL_BFLOAT16,
+                                         torch.cuda.current_stream(), ccl.LaunchConfig(stages=1)))
+    torch.cuda.synchronize()
+    for a, b in zip(got, y):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del g

@@ -118,11 +118,11 @@ def test_rejections():
         assert (b.base == b.fill).all().item()
 
 
-@pytest.mark.parametrize("stages", [1, 2])
+@pytest.mark.parametrize("stages", [1, 2, "split", "default"])
 def test_full_size_sampled_rows(stages):
     """P=8, 16384 tokens x 8192 hidden bf16 (256 MiB per rank): exact replica
     identity on the GPU and sampled rows against the oracle, one workgroup per
-    row and row-pipelined."""
+    row, row-pipelined, and split into 4 KiB pieces."""
     P, rows, hidden = 8, 16384, 8192
     dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=DEV)
     gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
@@ -130,7 +130,9 @@ def test_full_size_sampled_rows(stages):
     dy = [torch.empty_like(t) for t in dx]
     ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16,
                                          torch.cuda.current_stream(),
-                                         ccl.LaunchConfig(stages=stages)))
+                                         None if stages == "default"
+                                         else ccl.LaunchConfig(chunk_bytes=4096) if stages == "split"
+                                         else ccl.LaunchConfig(stages=stages)))
     torch.cuda.synchronize()
     for q in range(1, P):
         assert torch.equal(dy[q].view(torch.int16), dy[0].view(torch.int16))
@@ -140,3 +142,139 @@ def test_full_size_sampled_rows(stages):
     want = oracle.all_reduce_rmsnorm(xs, sample.size, hidden, gamma, 1e-6, "bf16")[0]
     got = dy[0].view(rows, hidden)[torch.from_numpy(sample).to(DEV)].view(torch.int16).cpu().numpy()
     assert_rmsnorm_parity(got.view(np.uint16).ravel(), want, "bf16", hidden, "full size")
+
+
+# ------------------------------------------------------------ split rows
+# chunk_bytes = 4096 cuts every row into 4 KiB pieces (one vector per lane):
+# a fold pass (one workgroup per piece) parks the folded row in the first
+# output and writes per-piece sums of squares, a norm pass scales and stores.
+
+SPLIT = dict(chunk_bytes=4096)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 5, 8, 9, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("row_bytes", [4112, 8192, 12304, 16384, 20496, 32768])
+def test_split_rows_match_oracle(P, dtype, row_bytes):
+    """Rows of 2..8 pieces, the last one full or holding a single vector."""
+    hidden = row_bytes // ESZ[dtype]
+    rows, eps = 37, 1e-6
+    xs = si.rank_buffers(P, rows * hidden, dtype, "normal", seed=P + row_bytes)
+    gamma = si.rank_buffers(1, hidden, dtype, "uniform", seed=8)[0]
+    print(f"split: P={P} {dtype} hidden={hidden}", flush=True)
+    got = run(xs, rows, hidden, gamma, eps, dtype, cfg=ccl.LaunchConfig(**SPLIT))
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, eps, dtype)
+    for q in range(P):
+        assert_rmsnorm_parity(got[q], want[q], dtype, hidden, f"split P={P} {dtype} H={hidden}")
+        np.testing.assert_array_equal(got[q], got[0])
+
+
+@pytest.mark.parametrize("cfg", [dict(), dict(occupancy=1), dict(occupancy=2), dict(nontemporal=4),
+                                 dict(store_policy=1), dict(nontemporal=1), dict(workgroups=3)])
+def test_split_launch_fields_do_not_change_results(cfg):
+    """Residency caps (both passes) and the cache hints leave the split
+    kernels' bits unchanged."""
+    P, rows, hidden = 8, 300, 16384
+    xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=12)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=13)[0]
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, 1e-6, "bf16")
+    base = run(xs, rows, hidden, gamma, 1e-6, "bf16", cfg=ccl.LaunchConfig(**SPLIT))
+    got = run(xs, rows, hidden, gamma, 1e-6, "bf16", cfg=ccl.LaunchConfig(**SPLIT, **cfg))
+    for q in range(P):
+        assert_rmsnorm_parity(base[q], want[q], "bf16", hidden, "split base")
+        np.testing.assert_array_equal(got[q], base[q])
+
+
+def test_split_in_place_repeated_calls_and_streams():
+    """In place; then calls back to back with new inputs, alternating between
+    the current stream and a second one (each stream has its own partial-sum
+    scratch)."""
+    P, rows, hidden = 4, 65, 8192
+    st = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=21)[0]
+    dg = DevBuf(gamma.nbytes, DEV).upload(gamma)
+    cfg = ccl.LaunchConfig(**SPLIT)
+    # in place
+    xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=20)
+    got = run(xs, rows, hidden, gamma, 1e-6, "bf16", in_place=True, cfg=cfg)
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, 1e-6, "bf16")
+    for q in range(P):
+        assert_rmsnorm_parity(got[q], want[q], "bf16", hidden, "split in place")
+    # five calls queued back to back, alternating streams, then checked
+    sets = [si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=30 + k) for k in range(5)]
+    dxs = [upload_all(x, DEV) for x in sets]
+    dys = [[DevBuf(rows * hidden * 2, DEV) for _ in range(P)] for _ in sets]
+    torch.cuda.synchronize()
+    for k, (dx, dy) in enumerate(zip(dxs, dys)):
+        s = side if k % 2 else st
+        ccl.check(ccl.ccl_all_reduce_rmsnorm([b.ptr for b in dx], [b.ptr for b in dy], P, rows,
+                                             hidden, dg.ptr, 1e-6, ccl.CCL_BFLOAT16, s, cfg))
+    torch.cuda.synchronize()
+    for k, (x, dy) in enumerate(zip(sets, dys)):
+        want = oracle.all_reduce_rmsnorm(x, rows, hidden, gamma, 1e-6, "bf16")
+        for q in range(P):
+            assert_rmsnorm_parity(dy[q].download(np.uint16), want[q], "bf16", hidden, f"call {k}")
+
+
+def test_split_many_pieces_in_flight():
+    """200,000 rows of 2 pieces (400,000 workgroups) in one call."""
+    P, rows, hidden = 2, 200_000, 4096
+    dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=5, device=DEV)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=6)[0]
+    dg = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
+    dy = [torch.empty_like(t) for t in dx]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16,
+                                         torch.cuda.current_stream(), ccl.LaunchConfig(**SPLIT)))
+    torch.cuda.synchronize()
+    assert torch.equal(dy[1].view(torch.int16), dy[0].view(torch.int16))
+    sample = si.sample_indices(rows, 96, seed=3).astype(np.int64)
+    it = torch.from_numpy(sample).to(DEV)
+    xs = [t.view(rows, hidden)[it].view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+          for t in dx]
+    want = oracle.all_reduce_rmsnorm(xs, sample.size, hidden, gamma, 1e-6, "bf16")[0]
+    got = dy[0].view(rows, hidden)[it].view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    assert_rmsnorm_parity(got, want, "bf16", hidden, "many pieces")
+
+
+def test_split_rejections():
+    P, rows, hidden = 2, 4, 4096
+    bufs = [DevBuf(rows * hidden * 2, DEV) for _ in range(2 * P)]
+    g = DevBuf(hidden * 2, DEV)
+    send, recv = [b.ptr for b in bufs[:P]], [b.ptr for b in bufs[P:]]
+    st = torch.cuda.current_stream()
+    for cfg in (dict(chunk_bytes=2048), dict(chunk_bytes=4096, stages=2)):
+        assert ccl.ccl_all_reduce_rmsnorm(send, recv, P, rows, hidden, g.ptr, 1e-6,
+                                          ccl.CCL_BFLOAT16, st,
+                                          ccl.LaunchConfig(**cfg)) == ccl.CCL_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    for b in bufs[P:]:
+        assert (b.base == b.fill).all().item()
+
+
+def test_default_split_writes_through_past_256mib_per_rank():
+    """P = 6 x 24576 x 8192 bf16 (384 MiB per rank): the default split form
+    writes through in its norm pass; the outputs equal the nontemporal-only
+    launch's bit for bit and the oracle on sampled rows."""
+    P, rows, hidden = 6, 24576, 8192
+    dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=4, device=DEV)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=5)[0]
+    dg = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
+    st = torch.cuda.current_stream()
+    dy = [torch.empty_like(t) for t in dx]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dy, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16, st))
+    dz = [torch.empty_like(t) for t in dx]
+    ccl.check(ccl.ccl_all_reduce_rmsnorm(dx, dz, P, rows, hidden, dg, 1e-6, ccl.CCL_BFLOAT16, st,
+                                         ccl.LaunchConfig(chunk_bytes=4096, store_policy=2)))
+    torch.cuda.synchronize()
+    for q in range(P):
+        assert torch.equal(dy[q].view(torch.int16), dz[q].view(torch.int16)), q
+        assert torch.equal(dy[q].view(torch.int16), dy[0].view(torch.int16)), q
+    del dz
+    sample = si.sample_indices(rows, 64, seed=9).astype(np.int64)
+    it = torch.from_numpy(sample).to(DEV)
+    xs = [t.view(rows, hidden)[it].view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+          for t in dx]
+    want = oracle.all_reduce_rmsnorm(xs, sample.size, hidden, gamma, 1e-6, "bf16")[0]
+    got = dy[0].view(rows, hidden)[it].view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    assert_rmsnorm_parity(got, want, "bf16", hidden, "default split, write-through")
