@@ -25,6 +25,7 @@ CCL_ERR_ALIASING = 3
 CCL_ERR_LAYOUT = 4
 CCL_ERR_HIP = 5
 CCL_ERR_NOMEM = 6
+CCL_ERR_SCRATCH_LIMIT = 7
 
 CCL_FLOAT32 = 0
 CCL_BFLOAT16 = 1
@@ -42,6 +43,7 @@ CCL_MAX_RANKS = 16
 CCL_MAX_MESH_DIMS = 4
 CCL_MAX_TENSOR_DIMS = 8
 CCL_MAX_MESH_RANKS = 64
+CCL_NOALLOC_SCRATCH_BYTES = 2 << 20
 
 DTYPES = {"f32": CCL_FLOAT32, "bf16": CCL_BFLOAT16, "i32": CCL_INT32, "f16": CCL_FLOAT16}
 OPS = {"sum": CCL_SUM, "min": CCL_MIN, "max": CCL_MAX}
@@ -85,7 +87,7 @@ _lib = None
 
 EXPORTS = [
     "ccl_all_reduce", "ccl_reduce_scatter", "ccl_all_gather", "ccl_reduce", "ccl_broadcast",
-    "ccl_all_reduce_rmsnorm",
+    "ccl_all_reduce_rmsnorm", "ccl_all_reduce_rmsnorm_noalloc",
     "ccl_reshard_plan",
     "ccl_reshard_copy", "ccl_reshard_copy_fp8", "ccl_plan_destroy", "ccl_plan_num_intervals", "ccl_plan_get_interval",
     "ccl_plan_local_bytes", "ccl_plan_num_dst_shards", "ccl_plan_shard_replicas",
@@ -114,6 +116,8 @@ def _load():
     lib.ccl_all_gather.argtypes = [pp, pp, i32, sz, i32, vp, pcfg]
     lib.ccl_reduce.argtypes = [pp, vp, i32, sz, i32, i32, i32, vp, pcfg]
     lib.ccl_all_reduce_rmsnorm.argtypes = [pp, pp, i32, sz, sz, vp, ctypes.c_float, i32, vp, pcfg]
+    lib.ccl_all_reduce_rmsnorm_noalloc.argtypes = [pp, pp, i32, sz, sz, vp, ctypes.c_float, i32, vp,
+                                                   pcfg]
     lib.ccl_broadcast.argtypes = [vp, pp, i32, sz, i32, i32, vp, pcfg]
     lib.ccl_reshard_plan.argtypes = [ctypes.POINTER(TensorDesc), ctypes.POINTER(Mesh),
                                      ctypes.POINTER(Placement), ctypes.POINTER(Mesh),
@@ -202,6 +206,14 @@ def ccl_all_reduce_rmsnorm(send, recv, nranks: int, rows: int, hidden: int, gamm
     s, r = _ptr_array(send), _ptr_array(recv)
     return _load().ccl_all_reduce_rmsnorm(_pp(s), _pp(r), nranks, rows, hidden, _addr(gamma),
                                           float(eps), dtype, _stream(stream), _cfg(cfg))
+
+
+def ccl_all_reduce_rmsnorm_noalloc(send, recv, nranks: int, rows: int, hidden: int, gamma,
+                                   eps: float, dtype: int, stream=None, cfg=None) -> int:
+    s, r = _ptr_array(send), _ptr_array(recv)
+    return _load().ccl_all_reduce_rmsnorm_noalloc(_pp(s), _pp(r), nranks, rows, hidden,
+                                                  _addr(gamma), float(eps), dtype, _stream(stream),
+                                                  _cfg(cfg))
 
 
 def ccl_reduce(send, recv, nranks: int, count: int, dtype: int, op: int, root: int = 0,

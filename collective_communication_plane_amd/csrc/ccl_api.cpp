@@ -140,6 +140,8 @@ const char *ccl_get_error_string(ccl_status_t s) {
     case CCL_ERR_LAYOUT: return "invalid reshard layout";
     case CCL_ERR_HIP: return "HIP runtime error";
     case CCL_ERR_NOMEM: return "out of memory";
+    case CCL_ERR_SCRATCH_LIMIT:
+      return "request needs more scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }
@@ -234,9 +236,15 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
 
-ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, int nranks,
-                                    size_t rows, size_t hidden, const void *gamma, float eps,
-                                    int dtype, void *stream, const ccl_launch_config_t *cfg) {
+}  // extern "C"
+
+namespace {
+
+// Both RMSNorm entry points; noalloc: the split-row kernels' partial sums go
+// to the fixed device array instead of the stream's library-allocated buffer.
+ccl_status_t ar_rmsnorm(const void *const *send, void *const *recv, int nranks, size_t rows,
+                        size_t hidden, const void *gamma, float eps, int dtype, void *stream,
+                        const ccl_launch_config_t *cfg, bool noalloc) {
   ccl::Launch l;
   ccl_status_t st = ccl::resolve_launch(cfg, ccl::OP_RMSNORM, nranks, &l);
   if (st) return st;
@@ -314,8 +322,31 @@ ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, 
   } else {
     l.occupancy2 = l.occupancy;
   }
+  void *part = nullptr;
+  if (split && noalloc) {
+    if (ccl::rms_split_scratch_bytes(rows, row_bytes) > ccl::kNoAllocScratchBytes)
+      return CCL_ERR_SCRATCH_LIMIT;
+    if ((st = ccl::noalloc_scratch(&part))) return st;
+  }
   ccl::RmsDesc d{nranks, dtype, rows, hidden, eps, send, recv, gamma};
-  return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream, split);
+  return ccl::launch_ar_rmsnorm(d, l, (hipStream_t)stream, split, part);
+}
+
+}  // namespace
+
+extern "C" {
+
+ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, int nranks,
+                                    size_t rows, size_t hidden, const void *gamma, float eps,
+                                    int dtype, void *stream, const ccl_launch_config_t *cfg) {
+  return ar_rmsnorm(send, recv, nranks, rows, hidden, gamma, eps, dtype, stream, cfg, false);
+}
+
+ccl_status_t ccl_all_reduce_rmsnorm_noalloc(const void *const *send, void *const *recv,
+                                            int nranks, size_t rows, size_t hidden,
+                                            const void *gamma, float eps, int dtype, void *stream,
+                                            const ccl_launch_config_t *cfg) {
+  return ar_rmsnorm(send, recv, nranks, rows, hidden, gamma, eps, dtype, stream, cfg, true);
 }
 
 ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t count, int dtype,

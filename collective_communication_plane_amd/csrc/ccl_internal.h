@@ -140,11 +140,15 @@ inline uint64_t rms_split_pieces(uint64_t row_bytes) {
 inline uint64_t rms_split_scratch_bytes(uint64_t rows, uint64_t row_bytes) {
   return rows * rms_split_pieces(row_bytes) * sizeof(float);
 }
-// split: run the split-row kernel.  Its scratch is `scratch` when given (at
-// least rms_split_scratch_bytes), else the calling stream's own buffer, which
-// the library allocates on first use and keeps.
+// split: run the split-row kernels.  Their partial sums go to part_buf when
+// given (at least rms_split_scratch_bytes), else to the calling stream's own
+// buffer, which the library allocates on first use and keeps.
 ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l, hipStream_t stream, bool split,
-                               void *scratch = nullptr);
+                               void *part_buf = nullptr);
+// The no-allocation entry point's fixed scratch (CCL_NOALLOC_SCRATCH_BYTES)
+// on the current device: its device address, looked up on first use.
+constexpr size_t kNoAllocScratchBytes = CCL_NOALLOC_SCRATCH_BYTES;
+ccl_status_t noalloc_scratch(void **out);
 
 // ------------------------------------------------------------------ reshard
 

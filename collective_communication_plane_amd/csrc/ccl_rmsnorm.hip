@@ -454,8 +454,34 @@ ccl_status_t stream_scratch(int dev, hipStream_t st, size_t need, void **out) {
 
 }  // namespace
 
+// The no-allocation entry point's partial sums: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process ends.
+// Its host-side name is not a device address; each device's address is looked
+// up once (hipGetSymbolAddress with that device current) and kept.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void *g_noalloc_addr[kMaxDevices];
+}  // namespace
+
+ccl_status_t noalloc_scratch(void **out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CCL_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_addr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return CCL_ERR_HIP;
+    g_noalloc_addr[dev] = ptr;
+  }
+  *out = g_noalloc_addr[dev];
+  return CCL_OK;
+}
+
 ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l_in, hipStream_t stream,
-                               bool split, void *scratch) {
+                               bool split, void *part_buf) {
   Launch l = l_in;
   RmsArgs a{};
   const int esz = dtype_size(d.dtype);
@@ -472,7 +498,7 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l_in, hipStream_t
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return CCL_ERR_HIP;
   const uint64_t row_bytes = (uint64_t)a.row_vecs * kVecBytes;
-  void *part = scratch;
+  void *part = part_buf;
   if (split && !part) {
     ccl_status_t st = stream_scratch(dev, stream, rms_split_scratch_bytes(d.rows, row_bytes), &part);
     if (st) return st;

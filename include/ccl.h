@@ -58,7 +58,9 @@ typedef enum {
     CCL_ERR_ALIASING = 3,    /* buffers overlap in a way the op cannot run in place */
     CCL_ERR_LAYOUT = 4,      /* reshard layout violates a constraint */
     CCL_ERR_HIP = 5,         /* a HIP runtime call failed */
-    CCL_ERR_NOMEM = 6        /* host or device allocation for library state failed */
+    CCL_ERR_NOMEM = 6,       /* host or device allocation for library state failed */
+    CCL_ERR_SCRATCH_LIMIT = 7 /* the no-allocation entry point would need more than
+                                 CCL_NOALLOC_SCRATCH_BYTES of scratch */
 } ccl_status_t;
 
 typedef enum { CCL_FLOAT32 = 0, CCL_BFLOAT16 = 1, CCL_INT32 = 2, CCL_FLOAT16 = 3 } ccl_dtype_t;
@@ -70,6 +72,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
 #define CCL_MAX_MESH_DIMS 4     /* axes of a reshard mesh */
 #define CCL_MAX_TENSOR_DIMS 8   /* dims of a resharded tensor */
 #define CCL_MAX_MESH_RANKS 64   /* ranks of one reshard mesh */
+#define CCL_NOALLOC_SCRATCH_BYTES (2u << 20) /* fixed scratch of the no-allocation entry point */
 
 /*
  * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
@@ -271,6 +274,27 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
 ccl_status_t ccl_all_reduce_rmsnorm(const void *const *send, void *const *recv, int nranks,
                                     size_t rows, size_t hidden, const void *gamma, float eps,
                                     int dtype, void *stream, const ccl_launch_config_t *cfg);
+
+/*
+ * ccl_all_reduce_rmsnorm for callers that cannot allocate device memory: code
+ * under stream capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, checks and results as ccl_all_reduce_rmsnorm (the same
+ * kernels, chosen by the same rules), but this call never allocates: the
+ * split-row form's partial sums (4 bytes per 4 KiB piece of a row, rows x
+ * ceil(hidden * element size / 4096) pieces) go to a fixed array of
+ * CCL_NOALLOC_SCRATCH_BYTES in device memory that the library holds, one copy
+ * per GPU, until the process ends.  A split-form call needing more returns
+ * CCL_ERR_SCRATCH_LIMIT and launches nothing (with 16 KiB rows: up to 131,072
+ * rows).  Every call on a GPU shares that GPU's array: calls that may overlap
+ * on one GPU (other streams, graph replays) race and must be ordered by the
+ * caller.  The array needs no clearing: a call reads only the sums its own
+ * first kernel wrote.  The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress), which allocates nothing.
+ */
+ccl_status_t ccl_all_reduce_rmsnorm_noalloc(const void *const *send, void *const *recv,
+                                            int nranks, size_t rows, size_t hidden,
+                                            const void *gamma, float eps, int dtype, void *stream,
+                                            const ccl_launch_config_t *cfg);
 
 /*
  * Reduce ([roadmap] GENK section: ring reduce; [digest] s2.2: shard-in with a

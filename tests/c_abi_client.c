@@ -106,7 +106,7 @@ int main(void) {
     int s;
 
     CHECK(ccl_version() > 0);
-    for (s = CCL_OK; s <= CCL_ERR_NOMEM; ++s) CHECK(ccl_get_error_string((ccl_status_t)s) != NULL);
+    for (s = CCL_OK; s <= CCL_ERR_SCRATCH_LIMIT; ++s) CHECK(ccl_get_error_string((ccl_status_t)s) != NULL);
 
     /* rejected before any HIP call: null buffers, bad rank counts, bad dtype */
     CHECK(ccl_all_reduce(send, recv, 2, 16, CCL_FLOAT32, CCL_SUM, NULL, NULL) ==
