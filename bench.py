@@ -26,9 +26,13 @@ Besides the headline value the line carries:
                 after a warmup of at least half a second.
 
 Other modes:
-  --sweep       the launch-configuration sweep (chunk bytes, stages, unroll,
-                resident workgroups per CU) for all-reduce, reduce-scatter
-                and all-gather at P=8 x 256 MiB bf16; one JSON line per point.
+  --sweep       the launch-configuration sweeps (chunk bytes, stages, unroll,
+                resident workgroups per CU): all-reduce at P=8 over 64 MiB,
+                256 MiB and 1 GiB per rank, bf16 and fp32, chunks 4 KiB ...
+                1 MiB; reduce-scatter and all-gather at P=8 x 256 MiB bf16; one
+                JSON line per point, then a table ranking the defaults.
+  --placements L  the headline all-reduce on one buffer layout (slab, alloc
+                or tensor), for rocprofv3 counter passes.
   --calibrate   also runs a plain 1 GiB device copy (torch) a few times, the
                 known-size reference that scales rocprofv3's FETCH_SIZE and
                 WRITE_SIZE counters to bytes.
@@ -38,7 +42,8 @@ Other modes:
                 from one HIP graph (no host work per call).
   --stores      the library default next to write-through (store_policy 1) and
                 nontemporal-only (2) stores on the bench workloads and the
-                sizes that set the write-through defaults; one JSON line each.
+                sizes that set the write-through defaults, including cold-MALL
+                forms (buffer sets used in turn); one JSON line each.
   --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
                 16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
                 same kernel), with the default and an uncapped occupancy, next
@@ -253,16 +258,18 @@ def cpu_baseline(seconds: float = 10.0):
                 return reps * 2 * P * n * 2 / el / 1e9, reps, el
 
     try:
-        T = min(16, len(os.sched_getaffinity(0)))
+        T = len(os.sched_getaffinity(0))  # every core this process may run on
     except AttributeError:
-        T = min(16, os.cpu_count() or 1)
+        T = os.cpu_count() or 1
     one, reps1, el1 = run(1, seconds / 2)
     many, repsT, elT = run(T, seconds / 2)
     return {"value": round(many, 3), "unit": "GB/s", "cores": T, "kind": "oracle",
-            "single_thread_value": round(one, 3),
+            "single_thread_value": round(one, 3), "host_cpus": os.cpu_count(),
+            "cpu_model": _cpu_model(),
             "sample": f"all_reduce sum over 8 ranks x 4,194,304 bf16 (first 8 MiB of the "
                       f"workload's shape, same distribution): {repsT} repetitions in {elT:.1f} s "
-                      f"on {T} threads, each running the oracle on its own slice; "
+                      f"on {T} threads (every core the process may use; the host has "
+                      f"{os.cpu_count()}), each running the oracle on its own slice; "
                       f"{reps1} repetitions in {el1:.1f} s on one thread; CPU {_cpu_model()}"}
 
 
@@ -317,6 +324,47 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     del sx, sy
     torch.cuda.empty_cache()
 
+    # Cold-MALL forms of the two workloads whose data fit the 256 MiB MALL
+    # between back-to-back calls (the all-gather's 256 MiB of input, the bf16
+    # reduce-scatter's 128 MiB of output): three buffer sets used in turn,
+    # each call touching data the two calls before it did not.
+    M = 16_777_216
+    sets = []
+    for k in range(3):
+        sx = si.device_rank_buffers(P, M, "bf16", "normal", seed=10 + k, device=dev)
+        sets.append((sx, [torch.empty(P * M * 2, dtype=torch.uint8, device=dev) for _ in range(P)]))
+    turn = [0]
+
+    def ag_cold():
+        x, y = sets[turn[0] % 3]
+        turn[0] += 1
+        ccl.check(ccl.ccl_all_gather(x, y, P, M, ccl.CCL_BFLOAT16, stream))
+
+    ms = timed(ag_cold, steps, warmup, stream, warm_s)
+    record("all_gather_bf16_cold", P * M * 2 + P * P * M * 2, ms,
+           "all_gather, P=8 x 16,777,216 bf16, three buffer sets used in turn (768 MiB of input, "
+           "6 GiB of output), so no call finds its input in the MALL")
+    del sets
+    torch.cuda.empty_cache()
+    N = 67_108_864
+    M = N // P
+    sets = []
+    for k in range(3):
+        sx = si.device_rank_buffers(P, N, "bf16", "normal", seed=20 + k, device=dev)
+        sets.append((sx, [torch.empty(M * 2, dtype=torch.uint8, device=dev) for _ in range(P)]))
+
+    def rs_cold():
+        x, y = sets[turn[0] % 3]
+        turn[0] += 1
+        ccl.check(ccl.ccl_reduce_scatter(x, y, P, M, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream))
+
+    ms = timed(rs_cold, steps, warmup, stream, warm_s)
+    record("reduce_scatter_bf16_cold", P * N * 2 + P * M * 2, ms,
+           "reduce_scatter sum, P=8 x 67,108,864 bf16, three buffer sets used in turn (3 GiB of "
+           "input, 384 MiB of output), so no call finds its output lines in the MALL")
+    del sets
+    torch.cuda.empty_cache()
+
     # the headline all-reduce with the caching allocator's placement (one
     # tensor per rank buffer), then through the LDS pipeline instead of VGPRs
     n = 134_217_728
@@ -327,6 +375,18 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     record("all_reduce_bf16_allocator_placement", 2 * P * n * 2, ms,
            "all_reduce sum, P=8 x 134,217,728 bf16, library defaults, one torch tensor per "
            "rank buffer (the caching allocator's placement)")
+    # ... and with all ranks in one [P, n] tensor (rank r at r x 256 MiB)
+    big_x = torch.empty(P, 2 * n, dtype=torch.uint8, device=dev)
+    for r in range(P):
+        big_x[r].copy_(dx[r].view(torch.uint8))
+    big_y = torch.empty_like(big_x)
+    bx, by = [big_x[r] for r in range(P)], [big_y[r] for r in range(P)]
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(bx, by, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                                    stream)), steps, warmup, stream, warm_s)
+    record("all_reduce_bf16_single_tensor", 2 * P * n * 2, ms,
+           "all_reduce sum, P=8 x 134,217,728 bf16, library defaults, the ranks as the rows of "
+           "one [8, n] tensor (256 MiB apart)")
+    del big_x, big_y, bx, by
     # the LDS pipeline on the headline's buffer layout (staggered slabs), so
     # that it compares with the headline's register-direct kernel
     sx, _ = rank_slab(P, 2 * n, dev)
@@ -343,6 +403,22 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
     del sx, sy
     torch.cuda.empty_cache()
 
+    # the all-reduce sweep's >= 64 MiB points (fp32 and bf16, 64 MiB and
+    # 1 GiB per rank) under the caching allocator's placement
+    for dt, code, esz in [("bf16", ccl.CCL_BFLOAT16, 2), ("f32", ccl.CCL_FLOAT32, 4)]:
+        for nbytes, tag in [(64 << 20, "64MiB"), (1 << 30, "1GiB")]:
+            cnt = nbytes // esz
+            cx = si.device_rank_buffers(P, cnt, dt, "uniform", seed=0, device=dev)
+            cy = [torch.empty_like(t) for t in cx]
+            ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(cx, cy, P, cnt, code, ccl.CCL_SUM,
+                                                            stream)), steps, warmup, stream,
+                       warm_s)
+            record(f"all_reduce_{dt}_{tag}", 2 * P * nbytes, ms,
+                   f"all_reduce sum, P=8 x {cnt:,} {dt} ({tag} per rank), library defaults, "
+                   "one torch tensor per rank buffer")
+            del cx, cy
+            torch.cuda.empty_cache()
+
     # all-reduce with RMSNorm fused between its halves: 16384 tokens x 8192 hidden
     rows, hidden = 16384, 8192
     dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=0, device=dev)
@@ -353,7 +429,20 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
                                                             ccl.CCL_BFLOAT16, stream)),
                steps, warmup, stream, warm_s)
     record("all_reduce_rmsnorm_bf16", 2 * P * rows * hidden * 2 + hidden * 2, ms,
-           "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16")
+           "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16 (split-row form), one "
+           "torch tensor per rank buffer")
+    # the same call with the ranks in staggered slabs, as in the headline
+    sx, _ = rank_slab(P, rows * hidden * 2, dev)
+    for d, t in zip(sx, dx):
+        d.copy_(t.view(torch.uint8))
+    sy, _ = rank_slab(P, rows * hidden * 2, dev)
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(sx, sy, P, rows, hidden, gamma, 1e-6,
+                                                            ccl.CCL_BFLOAT16, stream)),
+               steps, warmup, stream, warm_s)
+    record("all_reduce_rmsnorm_bf16_slab_placement", 2 * P * rows * hidden * 2 + hidden * 2, ms,
+           "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16 (split-row form), ranks in "
+           "staggered slabs as in the headline")
+    del sx, sy
     # the same bytes in 32 KiB rows, which take the row-pipelined kernel
     rows, hidden = 8192, 16384
     gamma = torch.from_numpy(si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
@@ -362,7 +451,7 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
                                                             ccl.CCL_BFLOAT16, stream)),
                steps, warmup, stream, warm_s)
     record("all_reduce_rmsnorm_bf16_long_rows", 2 * P * rows * hidden * 2 + hidden * 2, ms,
-           "all_reduce sum + RMSNorm per row, P=8 x 8192 x 16384 bf16 (row-pipelined)")
+           "all_reduce sum + RMSNorm per row, P=8 x 8192 x 16384 bf16 (split-row form)")
     del dx, dy
     torch.cuda.empty_cache()
 
@@ -422,24 +511,57 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
 
 
 def sweep(dev, stream) -> None:
-    """Launch-configuration sweep at P=8 x 256 MiB bf16 (sum); one JSON line each."""
+    """Launch-configuration sweeps; one JSON line per point, then a summary.
+
+    All-reduce at P=8 on the sweep workload's >= 64 MiB points (64 MiB,
+    256 MiB and 1 GiB per rank, bf16 and fp32, sum, one tensor per rank):
+    chunk bytes 4 KiB ... 1 MiB x stages 1 (register-direct, unroll 1 and 2)
+    and 2-4 (LDS pipeline) x resident workgroups per CU 2, 3, 4 and uncapped.
+    Reduce-scatter and all-gather at P=8 x 256 MiB bf16 over chunk bytes,
+    unroll, stages and residency.  The summary table ranks the library
+    default among the points of each workload."""
     import torch
 
     import synth_inputs as si
     from collective_communication_plane_amd import ccl
 
-    P, n = 8, 134_217_728
+    P = 8
+    results = []
+
+    def run(label, fn, nbytes, points):
+        for pt in points:
+            c = ccl.LaunchConfig(**pt) if pt else None
+            ms = timed(lambda: ccl.check(fn(c), label), 20, 3, stream, 0.05)
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rec = {"sweep": label, "config": pt or "default", "ms": round(ms, 5),
+                   "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            results.append(rec)
+            print(json.dumps(rec), flush=True)
+
+    chunks = [4096 << k for k in range(9)]  # 4 KiB ... 1 MiB
+    ar_points = [None]
+    for occ in (2, 3, 4, 32):
+        for chunk in chunks:
+            for unroll in (1, 2):
+                if chunk >= 4096 * unroll:
+                    ar_points.append(dict(chunk_bytes=chunk, unroll=unroll, stages=1,
+                                          occupancy=occ))
+            for stages in (2, 3, 4):
+                ar_points.append(dict(chunk_bytes=chunk, stages=stages, occupancy=occ))
+    for dt, code, esz in [("bf16", ccl.CCL_BFLOAT16, 2), ("f32", ccl.CCL_FLOAT32, 4)]:
+        for nbytes, tag in [(64 << 20, "64MiB"), (256 << 20, "256MiB"), (1 << 30, "1GiB")]:
+            n = nbytes // esz
+            dx = si.device_rank_buffers(P, n, dt, "uniform", seed=0, device=dev)
+            dy = [torch.empty_like(t) for t in dx]
+            run(f"all_reduce {dt} {tag}",
+                lambda c: ccl.ccl_all_reduce(dx, dy, P, n, code, ccl.CCL_SUM, stream, c),
+                2 * P * nbytes, ar_points)
+            del dx, dy
+            torch.cuda.empty_cache()
+
+    n = 134_217_728
     dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
     dy = [torch.empty(n * 2, dtype=torch.uint8, device=dev) for _ in range(P)]
-    ops = {
-        "all_reduce": (lambda c: ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
-                                                    stream, c), 2 * P * n * 2),
-        "reduce_scatter": (lambda c: ccl.ccl_reduce_scatter(dx, dy, P, n // P, ccl.CCL_BFLOAT16,
-                                                            ccl.CCL_SUM, stream, c),
-                           P * n * 2 + n * 2),
-        "all_gather": (lambda c: ccl.ccl_all_gather(dx, dy, P, n // P, ccl.CCL_BFLOAT16, stream, c),
-                       n * 2 + P * n * 2),
-    }
     points = [None]
     for occ in (1, 2, 3, 4, 32):
         for chunk in (4096, 8192, 16384, 65536):
@@ -448,18 +570,71 @@ def sweep(dev, stream) -> None:
                     points.append(dict(chunk_bytes=chunk, unroll=unroll, stages=1, occupancy=occ))
             for stages in (2, 3, 4):
                 points.append(dict(chunk_bytes=chunk, stages=stages, occupancy=occ))
-    for name, (fn, nbytes) in ops.items():
-        best = None
-        for pt in points:
-            c = ccl.LaunchConfig(**pt) if pt else None
-            ms = timed(lambda: ccl.check(fn(c), name), 20, 3, stream, 0.05)
-            gbs = nbytes / (ms * 1e-3) / 1e9
-            rec = {"sweep": name, "config": pt or "default", "ms": round(ms, 5),
-                   "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
-            print(json.dumps(rec), flush=True)
-            if best is None or gbs > best["GB/s"]:
-                best = rec
-        print(json.dumps({"sweep_best": name, **best}), flush=True)
+    run("reduce_scatter bf16 256MiB",
+        lambda c: ccl.ccl_reduce_scatter(dx, dy, P, n // P, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                         stream, c), P * n * 2 + n * 2, points)
+    run("all_gather bf16 256MiB",
+        lambda c: ccl.ccl_all_gather(dx, dy, P, n // P, ccl.CCL_BFLOAT16, stream, c),
+        n * 2 + P * n * 2, points)
+
+    # summary: per workload, the default's rank and the best point of each kind
+    print("| workload | default GB/s | default rank | best register-direct | "
+          "best LDS pipeline |")
+    print("|---|---|---|---|---|")
+    labels = []
+    for r in results:
+        if r["sweep"] not in labels:
+            labels.append(r["sweep"])
+    for lab in labels:
+        rs = sorted([r for r in results if r["sweep"] == lab], key=lambda r: -r["GB/s"])
+        d = next(r for r in rs if r["config"] == "default")
+        rank = rs.index(d) + 1
+
+        def best(kind):
+            b = next((r for r in rs if r["config"] != "default" and
+                      (r["config"]["stages"] == 1) == kind), None)
+            if b is None:
+                return "-"
+            c = b["config"]
+            what = (f"{c['chunk_bytes'] >> 10} KiB, unroll {c['unroll']}" if kind else
+                    f"{c['chunk_bytes'] >> 10} KiB, {c['stages']} stages")
+            occ = "uncapped" if c["occupancy"] == 32 else f"<= {c['occupancy']}/CU"
+            return f"{b['GB/s']} ({what}, {occ})"
+
+        print(f"| {lab} | {d['GB/s']} | {rank} of {len(rs)} | {best(True)} | {best(False)} |",
+              flush=True)
+
+
+def placements(dev, stream, layout: str, steps: int) -> None:
+    """The headline all-reduce (P=8 x 256 MiB bf16, library defaults) on one
+    buffer layout: "slab" (the headline's staggered slabs), "alloc" (one
+    torch tensor per rank buffer) or "tensor" (one [8, n] tensor); for
+    counter passes, one JSON line with the timed GB/s."""
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    P, n = 8, 134_217_728
+    src = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
+    if layout == "slab":
+        dx, _ = rank_slab(P, 2 * n, dev)
+        dy, _ = rank_slab(P, 2 * n, dev)
+        for d, t in zip(dx, src):
+            d.copy_(t.view(torch.uint8))
+    elif layout == "tensor":
+        bx = torch.empty(P, 2 * n, dtype=torch.uint8, device=dev)
+        by = torch.empty_like(bx)
+        for r in range(P):
+            bx[r].copy_(src[r].view(torch.uint8))
+        dx, dy = [bx[r] for r in range(P)], [by[r] for r in range(P)]
+    else:
+        dx, dy = src, [torch.empty_like(t) for t in src]
+    ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM,
+                                                    stream)), steps, 5, stream, 0.2)
+    gbs = 2 * P * n * 2 / (ms * 1e-3) / 1e9
+    print(json.dumps({"placement": layout, "steps": steps, "ms": round(ms, 5),
+                      "GB/s": round(gbs, 1)}), flush=True)
 
 
 def streams(dev, stream) -> None:
@@ -517,6 +692,46 @@ def stores(dev, stream) -> None:
 
     def bufs(P, nbytes):
         return [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(P)]
+
+    def rotating(fns):
+        """One launch function that uses the given ones in turn (cold-MALL forms:
+        each buffer set is touched again only after the others)."""
+        k = [0]
+
+        def fn(c):
+            k[0] += 1
+            return fns[k[0] % len(fns)](c)
+        return fn
+
+    # The all-gather and broadcast write-through rule (<= 256 MiB of input),
+    # re-checked cold: three buffer sets in turn, so no input is MALL-resident.
+    for P, M in ((8, 16_777_216), (4, 33_554_432), (12, 8_388_608)):
+        sets = [(si.device_rank_buffers(P, M, "bf16", "normal", seed=30 + k, device=dev),
+                 bufs(P, P * M * 2)) for k in range(3)]
+        fns = [lambda c, x=x, y=y: ccl.ccl_all_gather(x, y, P, M, ccl.CCL_BFLOAT16, stream, c)
+               for x, y in sets]
+        ab(f"all_gather P={P} x {M:,} bf16, cold (3 buffer sets in turn)", rotating(fns),
+           P * M * 2 * (1 + P))
+        del sets, fns
+        torch.cuda.empty_cache()
+    P, n = 8, (256 << 20) // 2
+    sets = [(si.device_rank_buffers(1, n, "bf16", "normal", seed=40 + k, device=dev)[0],
+             bufs(P, 2 * n)) for k in range(3)]
+    fns = [lambda c, x=x, y=y: ccl.ccl_broadcast(x, y, P, n, ccl.CCL_BFLOAT16, 0, stream, c)
+           for x, y in sets]
+    ab("broadcast P=8 x 256 MiB bf16, cold (3 buffer sets in turn)", rotating(fns),
+       2 * n * (P + 1))
+    del sets, fns
+    torch.cuda.empty_cache()
+    N = 67_108_864
+    sets = [(si.device_rank_buffers(P, N, "bf16", "normal", seed=50 + k, device=dev),
+             bufs(P, N // P * 2)) for k in range(3)]
+    fns = [lambda c, x=x, y=y: ccl.ccl_reduce_scatter(x, y, P, N // P, ccl.CCL_BFLOAT16,
+                                                      ccl.CCL_SUM, stream, c) for x, y in sets]
+    ab("reduce_scatter P=8 x 67,108,864 bf16, cold (3 buffer sets in turn)", rotating(fns),
+       P * N * 2 + N * 2)
+    del sets, fns
+    torch.cuda.empty_cache()
 
     P = 8
     for per_rank in (256 << 20, 1 << 30):  # the headline, and past the all-reduce's 256 MiB rule
@@ -668,6 +883,7 @@ def main() -> int:
     ap.add_argument("--streams", action="store_true")
     ap.add_argument("--sizes", action="store_true")
     ap.add_argument("--stores", action="store_true")
+    ap.add_argument("--placements", choices=["slab", "alloc", "tensor"])
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -698,6 +914,9 @@ def main() -> int:
         return 0
     if args.stores:
         stores(dev, stream)
+        return 0
+    if args.placements:
+        placements(dev, stream, args.placements, args.steps)
         return 0
     if args.calibrate:
         calibrate(dev)
@@ -747,7 +966,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
             "workload": "all_reduce sum, P=8 rank buffers x 134,217,728 bf16 (256 MiB) each, "

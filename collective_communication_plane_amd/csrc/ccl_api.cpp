@@ -90,7 +90,10 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
       l.stages_set = true;
     }
     if (cfg->unroll < 0 || cfg->unroll > 4 || cfg->unroll == 3) return CCL_ERR_INVALID_ARG;
-    if (cfg->unroll) l.unroll = cfg->unroll;
+    if (cfg->unroll) {
+      l.unroll = cfg->unroll;
+      l.unroll_set = true;
+    }
     if (cfg->nontemporal < 0 || cfg->nontemporal > 4) return CCL_ERR_INVALID_ARG;
     if (cfg->nontemporal == 4) {
       l.nt_load = l.nt_store = false;

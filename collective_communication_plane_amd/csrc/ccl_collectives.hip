@@ -89,7 +89,6 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   const DispatchFn dispatch = pick_dispatch(d.kind, d.dtype);
   CollPath p{};
   p.op = d.op;
-  p.unroll = l.unroll;
   p.stages = l.stages;
   p.occupancy = l.occupancy;
   p.nseg = nseg;
@@ -103,14 +102,40 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
   }
 
+  uint64_t chunk_bytes = l.chunk_bytes;
+  int occupancy = l.occupancy;
+  int unroll = l.unroll;
+  // All-reduce shapes by size and placement, from sweeps over P, per-rank
+  // size and three buffer layouts (bf16; one torch tensor per rank, the ranks
+  // in one [P, n] tensor, and staggered slabs):
+  //  - P = 8, 1-192 MiB per rank: 8 KiB chunks, unroll 2, <= 4 WGs per CU
+  //    (+7-12 % at 128 MiB and +8 % at 32 MiB on every layout, level at
+  //    64 MiB);
+  //  - 6 <= P <= 16 from 512 MiB per rank, when every input starts at the same
+  //    offset modulo 2 MiB (what separate framework allocations give): 16 KiB
+  //    chunks, <= 3 WGs per CU (+1-19 %).  Inputs staggered against each
+  //    other keep 4 KiB chunks, where 16 KiB ones lose 12-15 %.
+  if (d.kind == KIND_AR && !realign && l.stages <= 1 && !l.chunk_set && !l.occupancy_set &&
+      !l.unroll_set) {
+    const uint64_t per_rank = M * esz;
+    bool congruent = true;
+    for (int r = 1; r < d.P; ++r)
+      congruent = congruent && ((uintptr_t)a.in[r] - (uintptr_t)a.in[0]) % (uint64_t(2) << 20) == 0;
+    if (d.P == 8 && per_rank >= (uint64_t(1) << 20) && per_rank <= (uint64_t(192) << 20)) {
+      chunk_bytes = 8192;
+      unroll = 2;
+      occupancy = 4;
+    } else if (d.P >= 6 && per_rank >= (uint64_t(512) << 20) && congruent) {
+      chunk_bytes = 16384;
+      occupancy = 3;
+    }
+  }
   // The realigning kernel reads two blocks per input vector and wants other
   // chunks and residency than the aligned kernels whose defaults it would
   // otherwise inherit (reduce-scatter at P = 3 and 12: 2800-3200 GB/s under
   // those, 4800-5800 with these).  Its loads stay cacheable: a lane's second
   // block is its neighbour's first, which a nontemporal load does not keep
   // for it (the ragged reduce-scatter ran 4-15 % slower with them).
-  uint64_t chunk_bytes = l.chunk_bytes;
-  int occupancy = l.occupancy;
   if (realign) {
     const bool many = d.kind == KIND_RS && d.P > 8;
     if (!l.chunk_set) chunk_bytes = many ? 8192 : 4096;
@@ -121,11 +146,15 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // won in same-binary A/B runs on MI355X (bf16, separate kernel
   // instantiations): the reduce-scatter and reduce at P <= 8 (+3 % at P <= 4,
   // +1-8 % at P = 7, 8 from 64 to 512 MiB per rank; -0.3 to -0.8 % from
-  // P = 12); the all-gather and broadcast at P = 2 (+7 %) and, with >= 4
-  // resident workgroups per CU, at 4 <= P <= 12 when the whole input fits
-  // the 256 MiB MALL (+5 % to +30 %: written-through lines leave the input
-  // cached between calls; with 341-512 MiB of input they lose 2-6 %, at P = 3
-  // and P >= 13 they lose, with 3 workgroups per CU up to 30 %); the
+  // P = 12); the all-gather and broadcast at P = 2 (+7 %), at 7 <= P <= 12
+  // with at most 256 MiB of input and at 4 <= P <= 6 with at most 64 MiB, with
+  // >= 4 resident workgroups per CU.  That rule follows cold-MALL runs (three
+  // buffer sets used in turn): there write-through gains 1-21 % at P = 2 and
+  // 7-12, but at P = 4-6 with 128-256 MiB of input nontemporal-only stores
+  // win by 2-10 %.  (Repeating one call on the same buffers, the input stays
+  // in the MALL between calls and write-through gains up to 30 % more; with
+  // 341-512 MiB of input it loses 2-6 %, at P = 3 and P >= 13 it loses, with 3
+  // workgroups per CU up to 30 %.)  The
   // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank (P = 8:
   // +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at 128-256 MiB; P = 3-6 with
   // 341-682 MiB per rank: +2-11 % over the defaults, P = 3, 4 with 8 KiB
@@ -139,7 +168,8 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   if (!l.store_pol_set)
     wt = lines_aligned &&
          (d.kind == KIND_AG
-              ? (d.P == 2 || (d.P >= 4 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)))
+              ? (d.P == 2 || (d.P >= 7 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)) ||
+             (d.P >= 4 && d.P <= 6 && ag_in_bytes <= (uint64_t(64) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
                               : d.P >= 3 && d.P <= 8 && M * esz > (uint64_t(256) << 20));
   wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
@@ -150,6 +180,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     if (!l.occupancy_set) occupancy = 3;
   }
   p.occupancy = occupancy;
+  p.unroll = unroll;
   a.chunk_vecs = chunk_bytes / kVecBytes;
   a.chunks_per_seg = std::max<uint64_t>(1, (max_nvec + a.chunk_vecs - 1) / a.chunk_vecs);
   a.total_chunks = a.chunks_per_seg * nseg;

@@ -77,6 +77,7 @@ struct Launch {
   int occupancy;   // max resident workgroups per CU, 0 = no cap
   int occupancy2 = 0;  // the split-row RMSNorm's second (norm) pass
   bool chunk_set = false;      // chunk_bytes came from the caller
+  bool unroll_set = false;     // unroll came from the caller
   bool stages_set = false;     // stages came from the caller
   bool occupancy_set = false;  // occupancy came from the caller
   bool nt_set = false;         // nontemporal hints came from the caller

@@ -83,7 +83,12 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
  *                   write-through stores, past 256 MiB per rank: 8 KiB
  *                   chunks, <= 3 WGs per CU);
- *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU
+ *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but
+ *                   P = 8 with 1-192 MiB per rank: 8 KiB chunks, unroll 2,
+ *                   <= 4 WGs per CU; and 6 <= P <= 16 from 512 MiB per rank
+ *                   when every input starts at the same offset modulo 2 MiB
+ *                   (separate framework allocations): 16 KiB chunks, <= 3 WGs
+ *                   per CU
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
  *                   <= 4 WGs per CU for 9 <= P <= 12; for P = 7, 8 with more
@@ -165,9 +170,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                write-through for the all-reduce at 3 <= P <= 8 with more
  *                than 256 MiB per rank (at P = 3, 4 with 8 KiB chunks and
  *                <= 3 WGs per CU), for reduce-scatter and reduce at P <= 8, for
- *                all-gather and broadcast at P = 2, and at 4 <= P <= 12 with
- *                at most 256 MiB of input in all (from P = 9 on with <= 4 WGs
- *                per CU instead of 3), each only where every
+ *                all-gather and broadcast at P = 2, at 7 <= P <= 12 with at
+ *                most 256 MiB of input in all and at 4 <= P <= 6 with at most
+ *                64 MiB (from P = 9 on with <= 4 WGs per CU instead of 3),
+ *                each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
  *                only for the other all-reduces, the other all-gathers and
