@@ -33,6 +33,10 @@ Other modes:
                 JSON line per point, then a table ranking the defaults.
   --placements L  the headline all-reduce on one buffer layout (slab, alloc
                 or tensor), for rocprofv3 counter passes.
+  --defaults    the measurements behind the launch defaults, as markdown
+                tables (all-reduce by P, size and layout; reduce-scatter by P;
+                cold all-gather store policy by P; RMSNorm forms by P and row
+                length; reshard copy by replica count).
   --calibrate   also runs a plain 1 GiB device copy (torch) a few times, the
                 known-size reference that scales rocprofv3's FETCH_SIZE and
                 WRITE_SIZE counters to bytes.
@@ -814,6 +818,199 @@ def stores(dev, stream) -> None:
         torch.cuda.empty_cache()
 
 
+def defaults(dev, stream) -> None:
+    """The measurements behind the launch defaults, as markdown tables.
+
+    Each table puts the library default next to the alternatives its rule
+    chose between, in GB/s of algorithmic bytes (bf16):
+      A  all-reduce: P x bytes per rank x buffer layout ("alloc": one torch
+         tensor per rank, inputs at one offset modulo 2 MiB; "slab": ranks in
+         one allocation 256 MiB + 2 MiB + 4 KiB apart), launch shapes and
+         store policies;
+      B  reduce-scatter, 2 GiB of input over P ranks: shapes, LDS pipeline,
+         store policies; and P = 8 x 384 MiB with shards that are not whole
+         256-byte lines (where the LDS pipeline is the default);
+      C  all-gather and broadcast with a cold MALL (three buffer sets used in
+         turn): store policies by P and input size;
+      D  all-reduce + RMSNorm, 2 GiB of input: the split-row form against
+         the one-pass forms by P and row length;
+      E  reshard copy by replica count: chunk bytes, residency, cache hints.
+    """
+    import numpy as np
+    import torch
+
+    import synth_inputs as si
+    from collective_communication_plane_amd import ccl
+
+    def gbs(fn, nbytes, steps=12):
+        ms = timed(fn, steps, 3, stream, 0.03)
+        return nbytes / (ms * 1e-3) / 1e9
+
+    def table(title, header, rows):
+        print(f"\n### {title}\n", flush=True)
+        print("| " + " | ".join(header) + " |")
+        print("|" + "---|" * len(header))
+        for r in rows:
+            print("| " + " | ".join(f"{v:.0f}" if isinstance(v, float) else str(v) for v in r) +
+                  " |", flush=True)
+
+    def bufs(P, nbytes, layout):
+        if layout == "slab":
+            return rank_slab(P, nbytes, dev)[0]
+        return [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(P)]
+
+    L = ccl.LaunchConfig
+    # ---------------------------------------------------------------- A
+    shapes = [("default", None), ("4K u1 <=3", L(chunk_bytes=4096, unroll=1, occupancy=3)),
+              ("8K u2 <=4", L(chunk_bytes=8192, unroll=2, occupancy=4)),
+              ("16K u1 <=3", L(chunk_bytes=16384, unroll=1, occupancy=3)),
+              ("8K u1 <=8", L(chunk_bytes=8192, unroll=1, occupancy=8)),
+              ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
+    rows = []
+    for P in (2, 4, 6, 8, 12, 16):
+        for per_rank in (32 << 20, 128 << 20, 256 << 20, 512 << 20, 1 << 30):
+            for layout in ("alloc", "slab"):
+                x, y = bufs(P, per_rank, layout), bufs(P, per_rank, layout)
+                for b in x:
+                    b.view(torch.bfloat16).uniform_(-1, 1)
+                n = per_rank // 2
+                vals = [gbs(lambda: ccl.check(ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16,
+                                                                 ccl.CCL_SUM, stream, c)),
+                            2 * P * per_rank) for _, c in shapes]
+                rows.append([P, per_rank >> 20, layout, *vals])
+                del x, y
+                torch.cuda.empty_cache()
+    table("A. all-reduce bf16: P x MiB per rank x layout",
+          ["P", "MiB/rank", "layout"] + [k for k, _ in shapes], rows)
+
+    # ---------------------------------------------------------------- B
+    shapes = [("default", None),
+              ("8K u2 <=3", L(chunk_bytes=8192, unroll=2, occupancy=3, stages=1)),
+              ("4K u1 <=4", L(chunk_bytes=4096, unroll=1, occupancy=4, stages=1)),
+              ("4K u1 <=3", L(chunk_bytes=4096, unroll=1, occupancy=3, stages=1)),
+              ("LDS 2 stages <=2", L(chunk_bytes=8192, stages=2, occupancy=2)),
+              ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
+    rows = []
+    cases = [(P, (2 << 30) // (2 * P * P) // 128 * 128, 0) for P in (2, 4, 6, 8, 12, 16)]
+    # outputs that do not start on a 256-byte line (16 bytes past one), past
+    # 160 MiB of input per rank at P = 7, 8: where the LDS pipeline is the
+    # default, since write-through stores need whole lines
+    cases += [(8, (24 << 20) // 2, 16), (8, (32 << 20) // 2, 16), (8, (48 << 20) // 2, 16),
+              (7, (32 << 20) // 2, 16)]
+    for P, m, off in cases:
+        x = bufs(P, P * m * 2, "alloc")
+        yb = bufs(P, m * 2 + 256, "alloc")
+        y = [b[off:off + m * 2] for b in yb]
+        for b in x:
+            b.view(torch.bfloat16).uniform_(-1, 1)
+        vals = [gbs(lambda: ccl.check(ccl.ccl_reduce_scatter(x, y, P, m, ccl.CCL_BFLOAT16,
+                                                             ccl.CCL_SUM, stream, c)),
+                    P * P * m * 2 + P * m * 2) for _, c in shapes]
+        rows.append([P, f"{m * 2 / 2**20:.1f}", "no" if off else "yes", *vals])
+        del x, y, yb
+        torch.cuda.empty_cache()
+    table("B. reduce-scatter bf16 (one tensor per rank): P x MiB per output shard; the "
+          "register-direct columns set stages = 1",
+          ["P", "MiB/shard", "outputs on 256 B"] + [k for k, _ in shapes], rows)
+
+    # ---------------------------------------------------------------- C
+    rows = []
+    for P in (2, 3, 4, 5, 6, 7, 8, 10, 12, 16):
+        for total in (64 << 20, 256 << 20):
+            M = total // P // 2 // 128 * 128
+            sets = [(bufs(P, M * 2, "alloc"), bufs(P, P * M * 2, "alloc")) for _ in range(3)]
+            vals = []
+            for c in (None, L(store_policy=1), L(store_policy=2)):
+                k = [0]
+
+                def ag():
+                    x, y = sets[k[0] % 3]
+                    k[0] += 1
+                    ccl.check(ccl.ccl_all_gather(x, y, P, M, ccl.CCL_BFLOAT16, stream, c))
+                vals.append(gbs(ag, P * M * 2 * (1 + P), 24))
+            rows.append([P, P * M * 2 >> 20, *vals])
+            del sets
+            torch.cuda.empty_cache()
+    P, n = 8, (256 << 20) // 2
+    sets = [(torch.empty(2 * n, dtype=torch.uint8, device=dev), bufs(P, 2 * n, "alloc"))
+            for _ in range(3)]
+    vals = []
+    for c in (None, L(store_policy=1), L(store_policy=2)):
+        k = [0]
+
+        def bc():
+            x, y = sets[k[0] % 3]
+            k[0] += 1
+            ccl.check(ccl.ccl_broadcast(x, y, P, n, ccl.CCL_BFLOAT16, 0, stream, c))
+        vals.append(gbs(bc, 2 * n * (P + 1), 24))
+    rows.append(["8 (broadcast)", 256, *vals])
+    del sets
+    torch.cuda.empty_cache()
+    table("C. all-gather bf16, cold MALL (three buffer sets in turn): P x MiB of input",
+          ["P", "MiB in", "default", "write-through", "nontemporal"], rows)
+
+    # ---------------------------------------------------------------- D
+    shapes = [("default", None), ("one row per WG", L(stages=1)),
+              ("row-pipelined", L(stages=2)), ("split rows", L(chunk_bytes=4096))]
+    rows = []
+    for P in (4, 6, 8, 12):
+        for row_bytes in (4096, 8192, 16384, 24576, 32768):
+            hidden = row_bytes // 2
+            rows_n = (2 << 30) // P // row_bytes
+            x = bufs(P, rows_n * row_bytes, "alloc")
+            y = bufs(P, rows_n * row_bytes, "alloc")
+            for b in x:
+                b.view(torch.bfloat16).normal_()
+            g = torch.empty(hidden, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
+            vals = []
+            for name, c in shapes:
+                if name == "split rows" and row_bytes <= 4096:
+                    vals.append("-")
+                    continue
+                vals.append(gbs(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(
+                    x, y, P, rows_n, hidden, g, 1e-6, ccl.CCL_BFLOAT16, stream, c)),
+                    2 * P * rows_n * row_bytes + row_bytes))
+            rows.append([P, row_bytes >> 10, *vals])
+            del x, y
+            torch.cuda.empty_cache()
+    table("D. all-reduce + RMSNorm bf16, 2 GiB of input: P x KiB per row", ["P", "KiB/row"] +
+          [k for k, _ in shapes], rows)
+
+    # ---------------------------------------------------------------- E
+    shapes = [("default", None),
+              ("16K <=4 nt ld+st", L(chunk_bytes=16384, occupancy=4, nontemporal=3)),
+              ("32K <=2 nt st", L(chunk_bytes=32768, occupancy=2, nontemporal=2)),
+              ("32K <=2 nt ld+st", L(chunk_bytes=32768, occupancy=2, nontemporal=3)),
+              ("16K <=4 nt st", L(chunk_bytes=16384, occupancy=4, nontemporal=2)),
+              ("64K <=2 nt st", L(chunk_bytes=65536, occupancy=2, nontemporal=2))]
+    rows = []
+    for name, shape, src, dst, rho in [
+            ("weight [8192, 28672]", (8192, 28672), ([1, 4], 0, ["R", ("S", 0)]),
+             ([2, 2], 4, ["R", ("S", 0)]), 2),
+            ("MoE [64, 2048, 1408]", (64, 2048, 1408), ([8], 0, [("S", 0)]),
+             ([4], 8, [("S", 1)]), 1),
+            ("weight [8192, 28672] x 4 replicas", (8192, 28672), ([4], 0, [("S", 0)]),
+             ([4, 2], 4, ["R", ("S", 0)]), 4)]:
+        st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
+                                        ccl.make_mesh(src[0], src[1]), ccl.make_placements(src[2]),
+                                        ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))
+        ccl.check(st, "reshard_plan")
+        n_src, n_dst = int(np.prod(src[0])), int(np.prod(dst[0]))
+        tb = int(np.prod(shape)) * 2
+        dsrc = [torch.empty(tb // n_src, dtype=torch.uint8, device=dev) for _ in range(n_src)]
+        for b in dsrc:
+            b.view(torch.bfloat16).normal_()
+        ddst = [torch.empty(tb * rho // n_dst, dtype=torch.uint8, device=dev) for _ in range(n_dst)]
+        vals = [gbs(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream, c)),
+                    tb * (1 + rho)) for _, c in shapes]
+        rows.append([name, rho, *vals])
+        ccl.check(ccl.ccl_plan_destroy(plan))
+        del dsrc, ddst
+        torch.cuda.empty_cache()
+    table("E. reshard copy bf16: layout x replicas per destination shard",
+          ["layout", "replicas"] + [k for k, _ in shapes], rows)
+
+
 def sizes(dev, stream) -> None:
     """All-reduce at P=8 over per-rank sizes 4 KiB * 4^k (k = 0..9, up to 1 GiB),
     fp32 and bf16, sum / min / max, library defaults, ranks in staggered slabs;
@@ -884,6 +1081,7 @@ def main() -> int:
     ap.add_argument("--sizes", action="store_true")
     ap.add_argument("--stores", action="store_true")
     ap.add_argument("--placements", choices=["slab", "alloc", "tensor"])
+    ap.add_argument("--defaults", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -914,6 +1112,9 @@ def main() -> int:
         return 0
     if args.stores:
         stores(dev, stream)
+        return 0
+    if args.defaults:
+        defaults(dev, stream)
         return 0
     if args.placements:
         placements(dev, stream, args.placements, args.steps)

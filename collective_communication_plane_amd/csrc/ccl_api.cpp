@@ -284,11 +284,11 @@ ccl_status_t ar_rmsnorm(const void *const *send, void *const *recv, int nranks, 
   // shorter and longer ones uncapped.
   const uint64_t row_bytes = hidden * sz;
   // chunk_bytes below the row length asks for the split-row kernels, whose
-  // pieces are one vector per lane: 4 KiB per rank.  By default rows longer
-  // than 8 KiB per rank take them at P >= 6 (bf16, 2 GiB of input: +9-10 %
-  // at P = 8 on 16 KiB rows, +4-7 % on 32 KiB rows, +3-4 % at P = 6, +16 %
-  // at P = 12; they cost 1/P of the traffic extra, which loses at P <= 4, and
-  // break even on 8 KiB rows).
+  // pieces are one vector per lane: 4 KiB per rank.  By default rows of at
+  // least 8 KiB per rank take them at P >= 8 (bf16, 2 GiB of input: +1-9 %
+  // on 8 KiB rows, +8-13 % on 16 KiB rows, +3-10 % on 24-32 KiB rows at
+  // P = 8 and 12).  They move 1/P of the data twice more, which loses at
+  // P <= 4 and sits within the run-to-run spread at P = 6 (-3 % to +4 %).
   const uint64_t max_pieces = uint64_t(1) << 31;
   bool split = false;
   if (l.chunk_set && l.chunk_bytes < row_bytes) {
@@ -296,7 +296,7 @@ ccl_status_t ar_rmsnorm(const void *const *send, void *const *recv, int nranks, 
       return CCL_ERR_UNSUPPORTED;
     if (rows * ccl::rms_split_pieces(row_bytes) > max_pieces) return CCL_ERR_UNSUPPORTED;
     split = true;
-  } else if (!l.chunk_set && !l.stages_set && nranks >= 6 && row_bytes > 8192 &&
+  } else if (!l.chunk_set && !l.stages_set && nranks >= 8 && row_bytes >= 8192 &&
              rows * ccl::rms_split_pieces(row_bytes) <= max_pieces) {
     split = true;
   }
@@ -312,7 +312,10 @@ ccl_status_t ar_rmsnorm(const void *const *send, void *const *recv, int nranks, 
     l.store_wt = false;
   }
   if (split) l.store_pol_set = true;
-  if (!l.stages_set) l.stages = row_bytes > 16384 ? 2 : 1;
+  // One-pass forms: rows longer than 16 KiB take the row-pipelined kernel at
+  // P >= 6 (+1-5 % at 24-32 KiB); below P = 6 it loses up to 25 % to one
+  // workgroup per row.
+  if (!l.stages_set) l.stages = (row_bytes > 16384 && nranks >= 6) ? 2 : 1;
   if (!l.occupancy_set) {
     if (split) {
       l.occupancy = 4;   // fold pass

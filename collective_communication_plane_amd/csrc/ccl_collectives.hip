@@ -155,8 +155,9 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // in the MALL between calls and write-through gains up to 30 % more; with
   // 341-512 MiB of input it loses 2-6 %, at P = 3 and P >= 13 it loses, with 3
   // workgroups per CU up to 30 %.)  The
-  // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank (P = 8:
-  // +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at 128-256 MiB; P = 3-6 with
+  // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank, and at
+  // P <= 6 from 256 MiB (P = 8: +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at
+  // 128-256 MiB; P = 4 at 256 MiB: +19-22 %, P = 6: +2-7 %; P = 3-6 with
   // 341-682 MiB per rank: +2-11 % over the defaults, P = 3, 4 with 8 KiB
   // chunks and <= 3 workgroups per CU).  Only where every chunk's stores
   // start on a 256-byte boundary: the all-gather at P = 8 with shards of
@@ -164,6 +165,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // shard size that is not a multiple of 256 bytes lost 10-43 %.  The stores
   // address a chunk through a buffer resource with 31-bit offsets.
   const uint64_t ag_in_bytes = (uint64_t)(d.single ? 1 : d.P) * M * esz;
+  const uint64_t ar_wt_from = d.P <= 6 ? (uint64_t(256) << 20) : (uint64_t(256) << 20) + 1;
   bool wt = l.store_wt;
   if (!l.store_pol_set)
     wt = lines_aligned &&
@@ -171,7 +173,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
               ? (d.P == 2 || (d.P >= 7 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)) ||
              (d.P >= 4 && d.P <= 6 && ag_in_bytes <= (uint64_t(64) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
-                              : d.P >= 3 && d.P <= 8 && M * esz > (uint64_t(256) << 20));
+                              : d.P >= 3 && d.P <= 8 && M * esz >= ar_wt_from);
   wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;

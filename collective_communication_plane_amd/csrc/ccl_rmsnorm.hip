@@ -506,7 +506,7 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l_in, hipStream_t
       // in capture without scratch: the one-pass form this row length takes
       // by default (the same result within the documented bound, other bits)
       split = false;
-      l.stages = row_bytes > 16384 ? 2 : 1;
+      l.stages = (row_bytes > 16384 && d.P >= 6) ? 2 : 1;
       l.occupancy = l.stages == 2 ? 1 : (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
       l.store_wt = false;
     }

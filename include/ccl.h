@@ -81,7 +81,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
  *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
- *                   write-through stores, past 256 MiB per rank: 8 KiB
+ *                   write-through stores, from 256 MiB per rank: 8 KiB
  *                   chunks, <= 3 WGs per CU);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but
  *                   P = 8 with 1-192 MiB per rank: 8 KiB chunks, unroll 2,
@@ -107,16 +107,16 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   nontemporal stores only
  *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
- *   all-reduce + RMSNorm  P >= 6 with rows longer than 8 KiB per rank: the
- *                   split-row form (chunk_bytes = 4096 below): a fold pass
- *                   with <= 4 WGs per CU and a norm pass with <= 2, whose
- *                   stores write through past 256 MiB per rank when every
- *                   output and row starts on 256 bytes.  Otherwise rows of
- *                   up to 16 KiB per rank: one workgroup per row; <= 3 WGs
- *                   per CU for rows of 4-8 KiB, otherwise residency bounded
- *                   only by registers and the row buffer it keeps in LDS.
- *                   Longer rows: the row-pipelined kernel (stages = 2) on a
- *                   persistent grid of one workgroup per CU.  It reads
+ *   all-reduce + RMSNorm  P >= 8 with rows of at least 8 KiB per rank:
+ *                   the split-row form (chunk_bytes = 4096 below): a fold
+ *                   pass with <= 4 WGs per CU and a norm pass with <= 2,
+ *                   whose stores write through past 256 MiB per rank when
+ *                   every output and row starts on 256 bytes.  Otherwise
+ *                   one workgroup per row; <= 3 WGs per CU for rows of 4-8
+ *                   KiB, otherwise residency bounded only by registers and
+ *                   the row buffer it keeps in LDS; at P >= 6 rows longer
+ *                   than 16 KiB take the row-pipelined kernel (stages = 2)
+ *                   on a persistent grid of one workgroup per CU.  It reads
  *                   chunk_bytes (4096 or at least the row), workgroups,
  *                   stages (1 or 2; 3 and 4 give CCL_ERR_UNSUPPORTED),
  *                   nontemporal, occupancy (both passes of the split form)
@@ -168,7 +168,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
  *                write-through for the all-reduce at 3 <= P <= 8 with more
- *                than 256 MiB per rank (at P = 3, 4 with 8 KiB chunks and
+ *                than 256 MiB per rank, at 3 <= P <= 6 from 256 MiB (at
+ *                P = 3, 4 with 8 KiB chunks and
  *                <= 3 WGs per CU), for reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, at 7 <= P <= 12 with at
  *                most 256 MiB of input in all and at 4 <= P <= 6 with at most

@@ -253,10 +253,10 @@ def test_split_rejections():
 
 
 def test_default_split_writes_through_past_256mib_per_rank():
-    """P = 6 x 24576 x 8192 bf16 (384 MiB per rank): the default split form
+    """P = 8 x 24576 x 8192 bf16 (384 MiB per rank): the default split form
     writes through in its norm pass; the outputs equal the nontemporal-only
     launch's bit for bit and the oracle on sampled rows."""
-    P, rows, hidden = 6, 24576, 8192
+    P, rows, hidden = 8, 24576, 8192
     dx = si.device_rank_buffers(P, rows * hidden, "bf16", "normal", seed=4, device=DEV)
     gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=5)[0]
     dg = torch.from_numpy(gamma.view(np.int16).copy()).to(DEV)
@@ -278,3 +278,23 @@ def test_default_split_writes_through_past_256mib_per_rank():
     want = oracle.all_reduce_rmsnorm(xs, sample.size, hidden, gamma, 1e-6, "bf16")[0]
     got = dy[0].view(rows, hidden)[it].view(torch.int16).cpu().numpy().view(np.uint16).ravel()
     assert_rmsnorm_parity(got, want, "bf16", hidden, "default split, write-through")
+
+
+@pytest.mark.parametrize("P, hidden, split", [(8, 4096, True), (6, 8192, False), (4, 16384, False),
+                                              (12, 8192, True), (6, 12288, False)])
+def test_default_form_by_rank_count_and_row_length(P, hidden, split):
+    """The default launch picks the split-row form at P >= 8 for rows of at
+    least 8 KiB and a one-pass form otherwise: its bits equal those of the
+    explicitly requested form (the two forms add the sum of squares in
+    different orders), and the oracle's within the bar."""
+    rows = 23
+    xs = si.rank_buffers(P, rows * hidden, "bf16", "normal", seed=P + hidden)
+    gamma = si.rank_buffers(1, hidden, "bf16", "uniform", seed=3)[0]
+    got = run(xs, rows, hidden, gamma, 1e-6, "bf16")
+    one_pass = ccl.LaunchConfig(stages=2 if hidden * 2 > 16384 and P >= 6 else 1)
+    ref = run(xs, rows, hidden, gamma, 1e-6, "bf16",
+              cfg=ccl.LaunchConfig(chunk_bytes=4096) if split else one_pass)
+    want = oracle.all_reduce_rmsnorm(xs, rows, hidden, gamma, 1e-6, "bf16")
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], ref[q])
+        assert_rmsnorm_parity(got[q], want[q], "bf16", hidden, f"default P={P} H={hidden}")

@@ -62,7 +62,7 @@ def _both(P, rows, hidden, seed, stream, cfg=None):
 @pytest.mark.parametrize("P, hidden, cfg", [
     (8, 8192, None),                          # default split form (P >= 6, 16 KiB rows)
     (4, 8192, dict(chunk_bytes=4096)),        # split form by request
-    (6, 16384, dict(occupancy=1)),            # split form, 32 KiB rows, one workgroup per CU
+    (8, 16384, dict(occupancy=1)),            # split form, 32 KiB rows, one workgroup per CU
     (4, 8192, None),                          # one-pass form (needs no scratch)
 ])
 def test_noalloc_equals_regular_on_two_calls_in_a_row(P, hidden, cfg):
