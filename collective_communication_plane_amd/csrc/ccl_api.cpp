@@ -48,13 +48,6 @@ ccl_status_t check_outputs_disjoint(void *const *recv, int P, uint64_t bytes) {
 
 namespace ccl {
 
-bool write_through_default(const Launch &l, const void *const *outs, int n) {
-  if (!l.nt_store || (l.store_pol_set && !l.store_wt)) return false;
-  for (int i = 0; i < n; ++i)
-    if ((uintptr_t)outs[i] % 256) return false;
-  return true;
-}
-
 int device_cu_count(int dev) {
   static std::mutex mu;
   static int cached[64] = {0};
@@ -122,10 +115,7 @@ ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch
     *out = l;
     return CCL_OK;
   }
-  if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) {
-    if (explicit_stages) return CCL_ERR_INVALID_ARG;
-    l.stages = 1;
-  }
+  if (l.stages > 1 && l.chunk_bytes % kLdsTileBytes) return CCL_ERR_INVALID_ARG;
   *out = l;
   return CCL_OK;
 }
@@ -198,18 +188,6 @@ ccl_status_t ccl_reduce_scatter(const void *const *send, void *const *recv, int 
       Range x{(uintptr_t)send[r], (uintptr_t)send[r] + in_bytes};
       if (overlap(x, y) && y.lo != x.lo + (uint64_t)s * out_bytes) return CCL_ERR_ALIASING;
     }
-  // Past ~160 MiB per rank (at P = 7, 8) the LDS pipeline overtakes the
-  // register-direct kernel with nontemporal stores (at P = 8: 6.3 vs 6.0 TB/s
-  // at 192-256 MiB, while at 32-128 MiB the register-direct kernel leads by
-  // 6-9 %), but not the one with write-through stores (+4-13 % over the LDS
-  // pipeline at 192-512 MiB, bf16 and int32), which the launch takes where
-  // every output starts on 256 bytes.  From P = 9 on the register-direct
-  // kernel with its own defaults leads at every size.
-  if (nranks >= 7 && nranks <= 8 && in_bytes > (160ull << 20) &&
-      !ccl::write_through_default(l, recv, nranks)) {
-    if (!l.stages_set) l.stages = 2;
-    if (!l.occupancy_set) l.occupancy = 2;
-  }
   ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, recvcount, send, recv, false};
   return ccl::launch_collective(d, l, (hipStream_t)stream);
 }
@@ -375,12 +353,6 @@ ccl_status_t ccl_reduce(const void *const *send, void *recv, int nranks, size_t 
     Range y{(uintptr_t)recv, (uintptr_t)recv + bytes};
     Range x{(uintptr_t)send[r], (uintptr_t)send[r] + bytes};
     if (overlap(x, y) && x.lo != y.lo) return CCL_ERR_ALIASING;
-  }
-  // the reduce-scatter kernels' size rule (see ccl_reduce_scatter)
-  if (nranks >= 7 && nranks <= 8 && bytes > (160ull << 20) &&
-      !ccl::write_through_default(l, &recv, 1)) {
-    if (!l.stages_set) l.stages = 2;
-    if (!l.occupancy_set) l.occupancy = 2;
   }
   ccl::CollDesc d{ccl::KIND_RS, nranks, dtype, op, count, send, recv1, true};
   return ccl::launch_collective(d, l, (hipStream_t)stream);

@@ -112,10 +112,6 @@ int device_cu_count(int dev);
 
 ccl_status_t resolve_launch(const ccl_launch_config_t *cfg, Op op, int P, Launch *out);
 
-// Whether a reduce-scatter or reduce with these outputs takes write-through
-// stores by default (nontemporal stores on, not turned off by the caller, and
-// every output on a 256-byte boundary).
-bool write_through_default(const Launch &l, const void *const *outs, int n);
 ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t stream);
 
 // All-reduce with a row-wise RMSNorm between its halves, all checks passed.

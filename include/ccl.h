@@ -91,10 +91,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   per CU
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
- *                   <= 4 WGs per CU for 9 <= P <= 12; for P = 7, 8 with more
- *                   than 160 MiB per rank and outputs that do not all start on
- *                   256 bytes (so no write-through stores), the 2-stage LDS
- *                   pipeline with <= 2 WGs per CU
+ *                   <= 4 WGs per CU for 9 <= P <= 12
  *   broadcast       as all-gather
  *   all-gather      P <= 3: register-direct, 8 KiB chunks, unroll 2, <= 4
  *                   (P <= 2) or 3 WGs per CU; 4 <= P <= 8: register-direct,
@@ -133,9 +130,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   chunk_bytes  contiguous bytes of each rank buffer one workgroup owns per
  *                scheduling step (its share of a shard); a multiple of 16,
  *                at least 1024.  The LDS pipeline needs a multiple of its
- *                4096-byte tile: an explicit stages > 1 with another chunk
- *                size is rejected, a default LDS choice falls back to
- *                register-direct.
+ *                4096-byte tile: stages > 1 with another chunk size is
+ *                rejected.
  *   workgroups   grid size; chunks are dealt to workgroups round-robin.
  *                Default: one workgroup per chunk.
  *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS

@@ -493,7 +493,7 @@ def test_outputs_misaligned_to_each_other_use_elementwise_kernel():
 
 @pytest.mark.parametrize("P", [1, 2, 3, 4, 6, 8, 12, 16])
 def test_default_launch_for_every_rank_count(P):
-    """The defaults change with P (LDS pipeline for 7..12 ranks, different caps)."""
+    """The defaults change with P (chunk sizes, unroll, residency caps, store policy)."""
     m = 3 * 4096 + 8
     xs = si.rank_buffers(P, P * m, "bf16", "uniform", seed=P)
     got = run_rs(xs, "bf16", "sum")
