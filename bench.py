@@ -16,8 +16,8 @@ Besides the headline value the line carries:
                 8 TB/s, and the HBM traffic rocprofv3 counted for it (from the
                 committed counter summary, only while the kernel source still
                 matches the one the counters were taken on);
-  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload
-                (single thread);
+  cpu_baseline  the CPU oracle timed on a bounded sample of the same workload,
+                on one thread and on every core the process may use;
   rows          the other data-plane workloads (reduce-scatter bf16 and int32,
                 all-gather, the all-reduce under the allocator's placement and
                 through the LDS pipeline, the
@@ -1176,7 +1176,10 @@ def main() -> int:
             "hbm_bytes_per_step": bytes_per_step,
             "launch": "library defaults (register-direct, 4 KiB chunks, <= 3 workgroups per CU)",
             "placement": f"each side one allocation, rank r at r x {stride} bytes "
-                         f"(256 MiB + 2 MiB + 4 KiB apart)",
+                         f"(256 MiB + 2 MiB + 4 KiB apart); rows "
+                         f"all_reduce_bf16_allocator_placement and "
+                         f"all_reduce_bf16_single_tensor time the same call on framework "
+                         f"layouts, which run slower",
             "parity_spot_check": parity,
             "per_call_ms": per_call,
             "algbw_GBs": round(algbw, 1),

@@ -135,7 +135,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   workgroups   grid size; chunks are dealt to workgroups round-robin.
  *                Default: one workgroup per chunk.
  *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS
- *                pipeline: producer waves stream tiles into a ring of
+ *                pipeline (never chosen by default: on MI355X it trails the
+ *                register-direct kernel on every workload measured):
+ *                producer waves stream tiles into a ring of
  *                `stages` LDS buffers with asynchronous global->LDS loads,
  *                consumer waves fold and store them (clamped so the ring
  *                fits in 128 KiB).  The reshard copy is register-direct only.
@@ -175,7 +177,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                written through cost far more than they save); nontemporal
  *                only for the other all-reduces, the other all-gathers and
  *                broadcasts, the reshard copy, the FP8 reshard and the fused
- *                RMSNorm (within +-1.3 % of write-through, either sign).
+ *                RMSNorm's one-pass forms (within +-1.3 % of write-through,
+ *                either sign); the split-row RMSNorm as stated above.
  *                Write-through applies to the register-direct kernels only
  *                (not the LDS pipeline or the realigning kernel).  It needs
  *                >= 4 resident workgroups per CU to cover its longer store
