@@ -504,10 +504,12 @@ ccl_status_t launch_ar_rmsnorm(const RmsDesc &d, const Launch &l_in, hipStream_t
     if (st) return st;
     if (!part) {
       // in capture without scratch: the one-pass form this row length takes
-      // by default (the same result within the documented bound, other bits)
+      // by default (the same result within the documented bound, other bits);
+      // the stages and residency cap the caller set still apply
       split = false;
-      l.stages = (row_bytes > 16384 && d.P >= 6) ? 2 : 1;
-      l.occupancy = l.stages == 2 ? 1 : (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
+      if (!l.stages_set) l.stages = (row_bytes > 16384 && d.P >= 6) ? 2 : 1;
+      if (!l.occupancy_set)
+        l.occupancy = l.stages == 2 ? 1 : (row_bytes >= 4096 && row_bytes <= 8192) ? 3 : 0;
       l.store_wt = false;
     }
   }

@@ -77,7 +77,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
 /*
  * Optional launch configuration ([digest] s2.3: the bulk-copy engine's launch
  * configuration is tuned by a sweep).  Pass NULL for the built-in defaults,
- * which come from that sweep on MI355X (2 GiB of bf16 input over P ranks):
+ * which come from such sweeps on MI355X (2 GiB of bf16 input over P ranks,
+ * unless a rule names sizes; `python bench.py --defaults` and `--sweep`
+ * re-measure every rule below against its alternatives):
  *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
  *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
@@ -265,8 +267,9 @@ ccl_status_t ccl_all_gather(const void *const *send, void *const *recv, int nran
  * needs more allocates a larger one (at least twice the size), and every such
  * buffer is kept until the process ends.  A call made while its stream is
  * being captured cannot allocate: if the stream has no buffer large enough
- * yet, it runs the one-pass form instead (so make one eager call on the
- * capturing stream first to capture the split form).  A captured call keeps
+ * yet, it runs the one-pass form instead, with the caller's stages and
+ * occupancy where set (so make one eager call on the capturing stream first
+ * to capture the split form).  A captured call keeps
  * the buffer of the stream it was captured on: replaying the graph while
  * other calls run on that stream, or on two streams at once, races.
  *

@@ -199,3 +199,20 @@ def test_split_rmsnorm_in_a_graph_and_capture_fallback():
     for a, b in zip(got, y):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     del g
+
+    # the split form asked for explicitly, with a residency cap: captured on
+    # another fresh stream it falls back the same way and keeps the cap
+    cfg = ccl.LaunchConfig(chunk_bytes=4096, occupancy=1)
+    fresh2 = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=fresh2):
+        ccl.check(ccl.ccl_all_reduce_rmsnorm(x, y, P, rows, hidden, gamma, 1e-6,
+                                             ccl.CCL_BFLOAT16, torch.cuda.current_stream(), cfg))
+    torch.cuda.synchronize()
+    for o in y:
+        o.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    for a, b in zip(got, y):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    del g
