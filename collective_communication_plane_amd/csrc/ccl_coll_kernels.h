@@ -149,6 +149,21 @@ struct VecWaves {
 // WT: write-through stores (st_wt) as a compile-time choice, so that the
 // nontemporal / plain kernel stays exactly what it is without them (a runtime
 // branch among the three store paths slowed the nontemporal one).
+//
+// Cache hints.  With P nontemporal streams in flight, keeping exactly one of
+// them on the default (cacheable) policy measured several percent faster
+// than none and than two.  In the nontemporal paths below, slot 0 is that
+// stream: input 0's loads for the reduce-scatter, reduce, all-gather and
+// broadcast (their only input), output 0's stores for the all-reduce (the
+// host puts the last output into slot 0); an all-reduce whose stores write
+// through keeps input 0's loads cacheable instead, and one with two vectors
+// per lane in flight (U = 2) both (with U = 2, one cacheable stream ran 6 %
+// slower than the two).  The
+// nontemporal and the plain path of a group sit on the two sides of a branch
+// on a run-time flag; left alone, the compiler treats a nontemporal access
+// and a plain one to the same address there as one plain access, for
+// whichever accesses it happens to merge.  An empty volatile asm statement
+// (it emits nothing) at each end of a nontemporal group keeps them apart.
 template <int KIND, int DT, int OP, int PMAX, int U, bool WT>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(VecWaves<KIND, PMAX, U>::value)))
@@ -161,6 +176,13 @@ __global__ void __launch_bounds__(kThreads)
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
   const bool ntl = a.flags & 1, nts = a.flags & 2;
+  // compile-time: which slot-0 stream stays cacheable (see above)
+  constexpr bool pin0 = KIND != KIND_AR || WT || U > 1;
+  constexpr bool pout0 = KIND == KIND_AR;
+  // An all-reduce with U = 2 and nontemporal stores keeps the last rank's
+  // input cacheable (it measured 1-3 % ahead of rank 0's): slot 0 loads rank
+  // P - 1 and slot r rank r - 1, and the fold takes the slots in rank order.
+  constexpr bool rot = KIND == KIND_AR && U > 1 && !WT;
 
   for (uint64_t c = blockIdx.x; c < a.total_chunks; c += gridDim.x) {
     const int s = (int)(c / a.chunks_per_seg);
@@ -180,7 +202,9 @@ __global__ void __launch_bounds__(kThreads)
     const char *ib[NI];
     char *ob[NO];
 #pragma unroll
-    for (int r = 0; r < NI; ++r) ib[r] = r < ni ? in_at<KIND>(a, s, r, head, esz) : nullptr;
+    for (int r = 0; r < NI; ++r)
+      ib[r] = r >= ni ? nullptr
+                      : in_at<KIND>(a, s, !rot ? r : r == 0 ? ni - 1 : r - 1, head, esz);
 #pragma unroll
     for (int q = 0; q < NO; ++q) ob[q] = q < no ? out_at<KIND>(a, s, q, head, esz) : nullptr;
 
@@ -197,9 +221,13 @@ __global__ void __launch_bounds__(kThreads)
         const uint64_t vv = v + (uint64_t)u * kThreads;
         const bool live = vv < v1;
         if (ntl) {
+          // the cacheable slot-0 load goes last, after the hinted ones
+          asm volatile("");
 #pragma unroll
-          for (int r = 0; r < NI; ++r)
+          for (int r = pin0 ? 1 : 0; r < NI; ++r)
             x[u][r] = (live && r < ni) ? ld_nt(ib[r] + vv * kVecBytes) : zero;
+          asm volatile("");
+          if constexpr (pin0) x[u][0] = live ? ld_plain(ib[0] + vv * kVecBytes) : zero;
         } else {
 #pragma unroll
           for (int r = 0; r < NI; ++r)
@@ -212,15 +240,29 @@ __global__ void __launch_bounds__(kThreads)
         if (vv < v1) {
           u32x4 y;
           if constexpr (KIND == KIND_AG) y = x[u][0];
-          else y = fold_vec<DT, OP, NI>(x[u], ni);
+          else if constexpr (!rot) y = fold_vec<DT, OP, NI>(x[u], ni);
+          else {
+            // back in rank order: slot r + 1 holds rank r, slot 0 rank ni - 1
+            u32x4 xr[NI];
+#pragma unroll
+            for (int r = 0; r < NI; ++r) {
+              const int next = r + 1 < NI ? r + 1 : 0;  // in bounds at compile time
+              xr[r] = r + 1 < ni ? x[u][next] : x[u][0];
+            }
+            y = fold_vec<DT, OP, NI>(xr, ni);
+          }
           if constexpr (WT) {
 #pragma unroll
             for (int q = 0; q < NO; ++q)
               if (q < no) st_wt(ob[q] + v0 * kVecBytes, (vv - v0) * kVecBytes, y);
           } else if (nts) {
+            // the cacheable slot-0 store goes last, after the hinted ones
+            asm volatile("");
 #pragma unroll
-            for (int q = 0; q < NO; ++q)
+            for (int q = pout0 ? 1 : 0; q < NO; ++q)
               if (q < no) st_nt(ob[q] + vv * kVecBytes, y);
+            asm volatile("");
+            if constexpr (pout0) st_plain(ob[0] + vv * kVecBytes, y);
           } else {
 #pragma unroll
             for (int q = 0; q < NO; ++q)

@@ -183,6 +183,11 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   }
   p.occupancy = occupancy;
   p.unroll = unroll;
+  p.path = realign ? PATH_REALIGN : l.stages > 1 ? PATH_LDS : PATH_VEC;
+  // The all-reduce kernel keeps slot 0's output stream cacheable (see the
+  // kernel); the outputs are interchangeable, and the last one measured best
+  // in that role (1-2 % over the first under the allocator's placement).
+  if (d.kind == KIND_AR && d.P > 1) std::swap(a.out[0], a.out[d.P - 1]);
   a.chunk_vecs = chunk_bytes / kVecBytes;
   a.chunks_per_seg = std::max<uint64_t>(1, (max_nvec + a.chunk_vecs - 1) / a.chunk_vecs);
   a.total_chunks = a.chunks_per_seg * nseg;
@@ -191,7 +196,6 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   grid = std::min<uint64_t>(grid, 1u << 30);
   p.grid = (unsigned)grid;
   p.lds = occupancy_lds(occupancy, 0);
-  p.path = realign ? PATH_REALIGN : l.stages > 1 ? PATH_LDS : PATH_VEC;
   err = dispatch(a, p, stream);
   return err == hipSuccess ? CCL_OK : CCL_ERR_HIP;
 }
