@@ -447,7 +447,7 @@ def rows(dev, stream, steps: int, warmup: int, warm_s: float = 0.5):
            "all_reduce sum + RMSNorm per row, P=8 x 16384 x 8192 bf16 (split-row form), ranks in "
            "staggered slabs as in the headline")
     del sx, sy
-    # the same bytes in 32 KiB rows, which take the row-pipelined kernel
+    # the same bytes in 32 KiB rows (also the split-row form at P = 8)
     rows, hidden = 8192, 16384
     gamma = torch.from_numpy(si.rank_buffers(1, hidden, "bf16", "uniform", seed=1)[0]
                              .view(np.int16).copy()).to(dev)
