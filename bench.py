@@ -68,7 +68,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "achieved HBM GB/s (and % of roofline) for all_reduce P=8, 256 MB bf16"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "all_reduce_p8_256MiB_bf16_traffic.txt")
-KERNEL_SOURCES = ["ccl_coll_kernels.h", "ccl_coll_inst.hip", "ccl_device.h"]
+# the collective kernels and the launch rules that pick their instantiation
+KERNEL_SOURCES = ["ccl_coll_kernels.h", "ccl_coll_inst.hip", "ccl_device.h", "ccl_collectives.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -828,8 +829,8 @@ def defaults(dev, stream) -> None:
          one allocation 256 MiB + 2 MiB + 4 KiB apart), launch shapes and
          store policies;
       B  reduce-scatter, 2 GiB of input over P ranks: shapes, LDS pipeline,
-         store policies; and P = 8 x 384 MiB with shards that are not whole
-         256-byte lines (where the LDS pipeline is the default);
+         store policies; and P = 7, 8 with shards that are not whole 256-byte
+         lines (so the default cannot write through);
       C  all-gather and broadcast with a cold MALL (three buffer sets used in
          turn): store policies by P and input size;
       D  all-reduce + RMSNorm, 2 GiB of input: the split-row form against
@@ -846,13 +847,16 @@ def defaults(dev, stream) -> None:
         ms = timed(fn, steps, 3, stream, 0.03)
         return nbytes / (ms * 1e-3) / 1e9
 
-    def table(title, header, rows):
+    def table(title, header):
+        """A markdown table whose rows are printed as they are measured."""
         print(f"\n### {title}\n", flush=True)
         print("| " + " | ".join(header) + " |")
-        print("|" + "---|" * len(header))
-        for r in rows:
+        print("|" + "---|" * len(header), flush=True)
+
+        def row(r):
             print("| " + " | ".join(f"{v:.0f}" if isinstance(v, float) else str(v) for v in r) +
                   " |", flush=True)
+        return row
 
     def bufs(P, nbytes, layout):
         if layout == "slab":
@@ -866,7 +870,8 @@ def defaults(dev, stream) -> None:
               ("16K u1 <=3", L(chunk_bytes=16384, unroll=1, occupancy=3)),
               ("8K u1 <=8", L(chunk_bytes=8192, unroll=1, occupancy=8)),
               ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
-    rows = []
+    row = table("A. all-reduce bf16: P x MiB per rank x layout",
+                ["P", "MiB/rank", "layout"] + [k for k, _ in shapes])
     for P in (2, 4, 6, 8, 12, 16):
         for per_rank in (32 << 20, 128 << 20, 256 << 20, 512 << 20, 1 << 30):
             for layout in ("alloc", "slab"):
@@ -877,11 +882,9 @@ def defaults(dev, stream) -> None:
                 vals = [gbs(lambda: ccl.check(ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16,
                                                                  ccl.CCL_SUM, stream, c)),
                             2 * P * per_rank) for _, c in shapes]
-                rows.append([P, per_rank >> 20, layout, *vals])
+                row([P, per_rank >> 20, layout, *vals])
                 del x, y
                 torch.cuda.empty_cache()
-    table("A. all-reduce bf16: P x MiB per rank x layout",
-          ["P", "MiB/rank", "layout"] + [k for k, _ in shapes], rows)
 
     # ---------------------------------------------------------------- B
     shapes = [("default", None),
@@ -890,11 +893,14 @@ def defaults(dev, stream) -> None:
               ("4K u1 <=3", L(chunk_bytes=4096, unroll=1, occupancy=3, stages=1)),
               ("LDS 2 stages <=2", L(chunk_bytes=8192, stages=2, occupancy=2)),
               ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
-    rows = []
+    row = table("B. reduce-scatter bf16 (one tensor per rank): P x MiB per output shard; the "
+                "register-direct columns set stages = 1",
+                ["P", "MiB/shard", "outputs on 256 B"] + [k for k, _ in shapes])
     cases = [(P, (2 << 30) // (2 * P * P) // 128 * 128, 0) for P in (2, 4, 6, 8, 12, 16)]
     # outputs that do not start on a 256-byte line (16 bytes past one), past
-    # 160 MiB of input per rank at P = 7, 8: where the LDS pipeline is the
-    # default, since write-through stores need whole lines
+    # 160 MiB of input per rank at P = 7, 8: the cases where write-through
+    # stores, which need whole lines, are off and where the LDS pipeline was
+    # once the default
     cases += [(8, (24 << 20) // 2, 16), (8, (32 << 20) // 2, 16), (8, (48 << 20) // 2, 16),
               (7, (32 << 20) // 2, 16)]
     for P, m, off in cases:
@@ -906,15 +912,13 @@ def defaults(dev, stream) -> None:
         vals = [gbs(lambda: ccl.check(ccl.ccl_reduce_scatter(x, y, P, m, ccl.CCL_BFLOAT16,
                                                              ccl.CCL_SUM, stream, c)),
                     P * P * m * 2 + P * m * 2) for _, c in shapes]
-        rows.append([P, f"{m * 2 / 2**20:.1f}", "no" if off else "yes", *vals])
+        row([P, f"{m * 2 / 2**20:.1f}", "no" if off else "yes", *vals])
         del x, y, yb
         torch.cuda.empty_cache()
-    table("B. reduce-scatter bf16 (one tensor per rank): P x MiB per output shard; the "
-          "register-direct columns set stages = 1",
-          ["P", "MiB/shard", "outputs on 256 B"] + [k for k, _ in shapes], rows)
 
     # ---------------------------------------------------------------- C
-    rows = []
+    row = table("C. all-gather bf16, cold MALL (three buffer sets in turn): P x MiB of input",
+                ["P", "MiB in", "default", "write-through", "nontemporal"])
     for P in (2, 3, 4, 5, 6, 7, 8, 10, 12, 16):
         for total in (64 << 20, 256 << 20):
             M = total // P // 2 // 128 * 128
@@ -928,7 +932,7 @@ def defaults(dev, stream) -> None:
                     k[0] += 1
                     ccl.check(ccl.ccl_all_gather(x, y, P, M, ccl.CCL_BFLOAT16, stream, c))
                 vals.append(gbs(ag, P * M * 2 * (1 + P), 24))
-            rows.append([P, P * M * 2 >> 20, *vals])
+            row([P, P * M * 2 >> 20, *vals])
             del sets
             torch.cuda.empty_cache()
     P, n = 8, (256 << 20) // 2
@@ -943,16 +947,15 @@ def defaults(dev, stream) -> None:
             k[0] += 1
             ccl.check(ccl.ccl_broadcast(x, y, P, n, ccl.CCL_BFLOAT16, 0, stream, c))
         vals.append(gbs(bc, 2 * n * (P + 1), 24))
-    rows.append(["8 (broadcast)", 256, *vals])
+    row(["8 (broadcast)", 256, *vals])
     del sets
     torch.cuda.empty_cache()
-    table("C. all-gather bf16, cold MALL (three buffer sets in turn): P x MiB of input",
-          ["P", "MiB in", "default", "write-through", "nontemporal"], rows)
 
     # ---------------------------------------------------------------- D
     shapes = [("default", None), ("one row per WG", L(stages=1)),
               ("row-pipelined", L(stages=2)), ("split rows", L(chunk_bytes=4096))]
-    rows = []
+    row = table("D. all-reduce + RMSNorm bf16, 2 GiB of input: P x KiB per row",
+                ["P", "KiB/row"] + [k for k, _ in shapes])
     for P in (4, 6, 8, 12):
         for row_bytes in (4096, 8192, 16384, 24576, 32768):
             hidden = row_bytes // 2
@@ -970,11 +973,9 @@ def defaults(dev, stream) -> None:
                 vals.append(gbs(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(
                     x, y, P, rows_n, hidden, g, 1e-6, ccl.CCL_BFLOAT16, stream, c)),
                     2 * P * rows_n * row_bytes + row_bytes))
-            rows.append([P, row_bytes >> 10, *vals])
+            row([P, row_bytes >> 10, *vals])
             del x, y
             torch.cuda.empty_cache()
-    table("D. all-reduce + RMSNorm bf16, 2 GiB of input: P x KiB per row", ["P", "KiB/row"] +
-          [k for k, _ in shapes], rows)
 
     # ---------------------------------------------------------------- E
     shapes = [("default", None),
@@ -983,7 +984,8 @@ def defaults(dev, stream) -> None:
               ("32K <=2 nt ld+st", L(chunk_bytes=32768, occupancy=2, nontemporal=3)),
               ("16K <=4 nt st", L(chunk_bytes=16384, occupancy=4, nontemporal=2)),
               ("64K <=2 nt st", L(chunk_bytes=65536, occupancy=2, nontemporal=2))]
-    rows = []
+    row = table("E. reshard copy bf16: layout x replicas per destination shard",
+                ["layout", "replicas"] + [k for k, _ in shapes])
     for name, shape, src, dst, rho in [
             ("weight [8192, 28672]", (8192, 28672), ([1, 4], 0, ["R", ("S", 0)]),
              ([2, 2], 4, ["R", ("S", 0)]), 2),
@@ -1003,12 +1005,10 @@ def defaults(dev, stream) -> None:
         ddst = [torch.empty(tb * rho // n_dst, dtype=torch.uint8, device=dev) for _ in range(n_dst)]
         vals = [gbs(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream, c)),
                     tb * (1 + rho)) for _, c in shapes]
-        rows.append([name, rho, *vals])
+        row([name, rho, *vals])
         ccl.check(ccl.ccl_plan_destroy(plan))
         del dsrc, ddst
         torch.cuda.empty_cache()
-    table("E. reshard copy bf16: layout x replicas per destination shard",
-          ["layout", "replicas"] + [k for k, _ in shapes], rows)
 
 
 def sizes(dev, stream) -> None:
@@ -1174,7 +1174,8 @@ def main() -> int:
                         "uniform[-1,1) seed 0, fp32 fold in rank order, bf16 out",
             "P": P, "count": n, "storage_dtype": "bf16", "accumulate": "f32",
             "hbm_bytes_per_step": bytes_per_step,
-            "launch": "library defaults (register-direct, 4 KiB chunks, <= 3 workgroups per CU)",
+            "launch": "library defaults (register-direct, 4 KiB chunks, <= 3 workgroups per CU, "
+                      "write-through stores)",
             "placement": f"each side one allocation, rank r at r x {stride} bytes "
                          f"(256 MiB + 2 MiB + 4 KiB apart); rows "
                          f"all_reduce_bf16_allocator_placement and "

@@ -106,25 +106,30 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   int occupancy = l.occupancy;
   int unroll = l.unroll;
   // All-reduce shapes by size and placement, from sweeps over P, per-rank
-  // size and three buffer layouts (bf16; one torch tensor per rank, the ranks
-  // in one [P, n] tensor, and staggered slabs):
-  //  - P = 8, 1-192 MiB per rank: 8 KiB chunks, unroll 2, <= 4 WGs per CU
-  //    (+7-12 % at 128 MiB and +8 % at 32 MiB on every layout, level at
-  //    64 MiB);
+  // size and buffer layout (bf16; one torch tensor per rank and staggered
+  // slabs, interleaved repeats):
+  //  - 3 <= P <= 8 with 1-128 MiB per rank: 8 KiB chunks, unroll 2, <= 4 WGs
+  //    per CU (+1.4-13.5 % at 32-128 MiB over the per-P shapes; past 128 MiB
+  //    per rank the shape falls off, -7 to -16 % from 144-320 MiB by P);
+  //  - P = 2 with 129-256 MiB per rank: unroll 1 (+11.5-17 % at 160-256 MiB;
+  //    level at 128 MiB, -1 to -7 % from 288 MiB);
   //  - 6 <= P <= 16 from 512 MiB per rank, when every input starts at the same
   //    offset modulo 2 MiB (what separate framework allocations give): 16 KiB
   //    chunks, <= 3 WGs per CU (+1-19 %).  Inputs staggered against each
   //    other keep 4 KiB chunks, where 16 KiB ones lose 12-15 %.
+  const uint64_t per_rank = M * esz;
   if (d.kind == KIND_AR && !realign && l.stages <= 1 && !l.chunk_set && !l.occupancy_set &&
       !l.unroll_set) {
-    const uint64_t per_rank = M * esz;
     bool congruent = true;
     for (int r = 1; r < d.P; ++r)
       congruent = congruent && ((uintptr_t)a.in[r] - (uintptr_t)a.in[0]) % (uint64_t(2) << 20) == 0;
-    if (d.P == 8 && per_rank >= (uint64_t(1) << 20) && per_rank <= (uint64_t(192) << 20)) {
+    if (d.P >= 3 && d.P <= 8 && per_rank >= (uint64_t(1) << 20) &&
+        per_rank <= (uint64_t(128) << 20)) {
       chunk_bytes = 8192;
       unroll = 2;
       occupancy = 4;
+    } else if (d.P == 2 && per_rank > (uint64_t(128) << 20) && per_rank <= (uint64_t(256) << 20)) {
+      unroll = 1;
     } else if (d.P >= 6 && per_rank >= (uint64_t(512) << 20) && congruent) {
       chunk_bytes = 16384;
       occupancy = 3;
@@ -155,17 +160,24 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // in the MALL between calls and write-through gains up to 30 % more; with
   // 341-512 MiB of input it loses 2-6 %, at P = 3 and P >= 13 it loses, with 3
   // workgroups per CU up to 30 %.)  The
-  // all-reduce only at 3 <= P <= 8 with more than 256 MiB per rank, and at
-  // P <= 6 from 256 MiB (P = 8: +1-7.5 % at 384 MiB to 1 GiB, -2.5 to -7 % at
-  // 128-256 MiB; P = 4 at 256 MiB: +19-22 %, P = 6: +2-7 %; P = 3-6 with
-  // 341-682 MiB per rank: +2-11 % over the defaults, P = 3, 4 with 8 KiB
-  // chunks and <= 3 workgroups per CU).  Only where every chunk's stores
+  // all-reduce, past the range of the 8 KiB / unroll-2 shape above: at P = 2
+  // above 256 MiB per rank (+1-6 % at 384 MiB to 1 GiB), at 3 <= P <= 6 from
+  // 256 MiB (P = 4 at 256 MiB: +19-22 % before the input-0 cacheable stream,
+  // level after it; P = 3-6 with 341-682 MiB per rank: +2-11 %, P = 3, 4 with
+  // 8 KiB chunks and <= 3 workgroups per CU; P = 3 loses 3-6 % at
+  // 128-192 MiB), at P = 7, 8 above 128 MiB (+2-11 % at 136 MiB to 1 GiB,
+  // +3-4 % at the P = 8 x 256 MiB point), and at 9 <= P <= 16 from 16 MiB
+  // (+0.5-8 % at 16-256 MiB and up to 1 GiB, one cell at -0.1 %).  Only
+  // where every chunk's stores
   // start on a 256-byte boundary: the all-gather at P = 8 with shards of
   // 2^24 + 8 elements ran 4086 GB/s with them against 5166 without, and every
   // shard size that is not a multiple of 256 bytes lost 10-43 %.  The stores
   // address a chunk through a buffer resource with 31-bit offsets.
   const uint64_t ag_in_bytes = (uint64_t)(d.single ? 1 : d.P) * M * esz;
-  const uint64_t ar_wt_from = d.P <= 6 ? (uint64_t(256) << 20) : (uint64_t(256) << 20) + 1;
+  const uint64_t ar_wt_from = d.P == 2   ? (uint64_t(256) << 20) + 1
+                              : d.P <= 6  ? (uint64_t(256) << 20)
+                              : d.P <= 8  ? (uint64_t(128) << 20) + 1
+                                          : (uint64_t(16) << 20);
   bool wt = l.store_wt;
   if (!l.store_pol_set)
     wt = lines_aligned &&
@@ -173,7 +185,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
               ? (d.P == 2 || (d.P >= 7 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)) ||
              (d.P >= 4 && d.P <= 6 && ag_in_bytes <= (uint64_t(64) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
-                              : d.P >= 3 && d.P <= 8 && M * esz >= ar_wt_from);
+                              : d.P >= 2 && per_rank >= ar_wt_from);
   wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;

@@ -81,16 +81,17 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  * unless a rule names sizes; `python bench.py --defaults` and `--sweep`
  * re-measure every rule below against its alternatives):
  *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
- *                   P = 2: 8 KiB chunks, unroll 2, <= 8 WGs per CU;
+ *                   P = 2: 8 KiB chunks, unroll 2 (unroll 1 above 128 and
+ *                   up to 256 MiB per rank), <= 8 WGs per CU (<= 3 with
+ *                   write-through stores);
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
- *                   write-through stores, from 256 MiB per rank: 8 KiB
- *                   chunks, <= 3 WGs per CU);
+ *                   write-through stores: 8 KiB chunks, <= 3 WGs per CU);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but
- *                   P = 8 with 1-192 MiB per rank: 8 KiB chunks, unroll 2,
- *                   <= 4 WGs per CU; and 6 <= P <= 16 from 512 MiB per rank
- *                   when every input starts at the same offset modulo 2 MiB
- *                   (separate framework allocations): 16 KiB chunks, <= 3 WGs
- *                   per CU
+ *                   3 <= P <= 8 with 1-128 MiB per rank: 8 KiB chunks,
+ *                   unroll 2, <= 4 WGs per CU; and 6 <= P <= 16 from 512 MiB
+ *                   per rank when every input starts at the same offset
+ *                   modulo 2 MiB (separate framework allocations): 16 KiB
+ *                   chunks, <= 3 WGs per CU
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
  *                   <= 4 WGs per CU for 9 <= P <= 12
@@ -174,10 +175,10 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                collectives, reshard copy, FP8 reshard codes and fused
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
- *                write-through for the all-reduce at 3 <= P <= 8 with more
- *                than 256 MiB per rank, at 3 <= P <= 6 from 256 MiB (at
- *                P = 3, 4 with 8 KiB chunks and
- *                <= 3 WGs per CU), for reduce-scatter and reduce at P <= 8, for
+ *                write-through for the all-reduce at P = 2 above 256 MiB
+ *                per rank, at 3 <= P <= 6 from 256 MiB, at P = 7, 8 above
+ *                128 MiB and at 9 <= P <= 16 from 16 MiB, for
+ *                reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, at 7 <= P <= 12 with at
  *                most 256 MiB of input in all and at 4 <= P <= 6 with at most
  *                64 MiB (from P = 9 on with <= 4 WGs per CU instead of 3),
