@@ -843,7 +843,7 @@ def defaults(dev, stream) -> None:
     import synth_inputs as si
     from collective_communication_plane_amd import ccl
 
-    def gbs(fn, nbytes, steps=12):
+    def gbs(fn, nbytes, steps=20):
         ms = timed(fn, steps, 3, stream, 0.03)
         return nbytes / (ms * 1e-3) / 1e9
 
@@ -872,8 +872,8 @@ def defaults(dev, stream) -> None:
               ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
     row = table("A. all-reduce bf16: P x MiB per rank x layout",
                 ["P", "MiB/rank", "layout"] + [k for k, _ in shapes])
-    for P in (2, 4, 6, 8, 12, 16):
-        for per_rank in (32 << 20, 128 << 20, 256 << 20, 512 << 20, 1 << 30):
+    for P in (2, 3, 4, 5, 6, 7, 8, 9, 12, 16):
+        for per_rank in (32 << 20, 64 << 20, 128 << 20, 192 << 20, 256 << 20, 512 << 20, 1 << 30):
             for layout in ("alloc", "slab"):
                 x, y = bufs(P, per_rank, layout), bufs(P, per_rank, layout)
                 for b in x:

@@ -150,16 +150,16 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // Write-through stores (register-direct kernel only), by default where they
   // won in same-binary A/B runs on MI355X (bf16, separate kernel
   // instantiations): the reduce-scatter and reduce at P <= 8 (+3 % at P <= 4,
-  // +1-8 % at P = 7, 8 from 64 to 512 MiB per rank; -0.3 to -0.8 % from
-  // P = 12); the all-gather and broadcast at P = 2 (+7 %), at 7 <= P <= 12
+  // +1-8 % at P = 7, 8 from 64 to 512 MiB per rank; -0.4 to +0.8 % from
+  // P = 9); the all-gather and broadcast at P = 2 (+7 %), at 7 <= P <= 16
   // with at most 256 MiB of input and at 4 <= P <= 6 with at most 64 MiB, with
-  // >= 4 resident workgroups per CU.  That rule follows cold-MALL runs (three
-  // buffer sets used in turn): there write-through gains 1-21 % at P = 2 and
-  // 7-12, but at P = 4-6 with 128-256 MiB of input nontemporal-only stores
-  // win by 2-10 %.  (Repeating one call on the same buffers, the input stays
-  // in the MALL between calls and write-through gains up to 30 % more; with
-  // 341-512 MiB of input it loses 2-6 %, at P = 3 and P >= 13 it loses, with 3
-  // workgroups per CU up to 30 %.)  The
+  // >= 4 resident workgroups per CU from P = 9 on.  That rule follows
+  // cold-MALL runs (three buffer sets used in turn): there write-through gains
+  // 1-21 % at P = 2 and 7-12 and 1-5 % at P = 13-16, but at P = 4-6 with
+  // 128-256 MiB of input nontemporal-only stores win by 2-10 %.  (Repeating
+  // one call on the same buffers, the input stays in the MALL between calls
+  // and write-through gains up to 30 % more; with 341-512 MiB of input it
+  // loses 2-6 %, at P = 3 it loses, with 3 workgroups per CU up to 30 %.)  The
   // all-reduce, past the range of the 8 KiB / unroll-2 shape above: at P = 2
   // above 256 MiB per rank (+1-6 % at 384 MiB to 1 GiB), at 3 <= P <= 6 from
   // 256 MiB (P = 4 at 256 MiB: +19-22 % before the input-0 cacheable stream,
@@ -182,7 +182,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   if (!l.store_pol_set)
     wt = lines_aligned &&
          (d.kind == KIND_AG
-              ? (d.P == 2 || (d.P >= 7 && d.P <= 12 && ag_in_bytes <= (uint64_t(256) << 20)) ||
+              ? (d.P == 2 || (d.P >= 7 && ag_in_bytes <= (uint64_t(256) << 20)) ||
              (d.P >= 4 && d.P <= 6 && ag_in_bytes <= (uint64_t(64) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
                               : d.P >= 2 && per_rank >= ar_wt_from);

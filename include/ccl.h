@@ -179,7 +179,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                per rank, at 3 <= P <= 6 from 256 MiB, at P = 7, 8 above
  *                128 MiB and at 9 <= P <= 16 from 16 MiB, for
  *                reduce-scatter and reduce at P <= 8, for
- *                all-gather and broadcast at P = 2, at 7 <= P <= 12 with at
+ *                all-gather and broadcast at P = 2, at 7 <= P <= 16 with at
  *                most 256 MiB of input in all and at 4 <= P <= 6 with at most
  *                64 MiB (from P = 9 on with <= 4 WGs per CU instead of 3),
  *                each only where every
