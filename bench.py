@@ -59,6 +59,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -72,11 +73,19 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "all_reduce_p8_256MiB_bf16_traf
 KERNEL_SOURCES = ["ccl_coll_kernels.h", "ccl_coll_inst.hip", "ccl_device.h", "ccl_collectives.hip"]
 
 
+def code_only(text: str) -> str:
+    """C++ source without its comments and with runs of whitespace collapsed, so
+    that editing a comment does not count as a change of the compiled code."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "collective_communication_plane_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "collective_communication_plane_amd", "csrc", name)) as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

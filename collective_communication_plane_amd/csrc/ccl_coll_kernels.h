@@ -153,15 +153,15 @@ struct VecWaves {
 // Cache hints.  With P nontemporal streams in flight, keeping exactly one of
 // them on the default (cacheable) policy measured several percent faster
 // than none and than two.  In the nontemporal paths below, slot 0 is that
-// stream: input 0's loads for the reduce-scatter, reduce, all-gather and
-// broadcast (their only input), output 0's stores for the all-reduce (the
-// host puts the last output into slot 0); an all-reduce whose stores write
-// through keeps input 0's loads cacheable instead, and one with two vectors
-// per lane in flight (U = 2) both (with U = 2, one cacheable stream ran 6 %
-// slower than the two).  The
-// nontemporal and the plain path of a group sit on the two sides of a branch
-// on a run-time flag; left alone, the compiler treats a nontemporal access
-// and a plain one to the same address there as one plain access, for
+// stream:
+//  - reduce-scatter, reduce, all-gather and broadcast: input 0's loads;
+//  - all-reduce: output 0's stores (the host puts the last output there);
+//  - all-reduce with write-through stores: input 0's loads instead;
+//  - all-reduce with two vectors per lane in flight (U = 2): input and output
+//    (one cacheable stream ran 6 % slower than the two there).
+// The nontemporal and the plain path of a group sit on the two sides of a
+// branch on a run-time flag.  Left alone, the compiler treats a nontemporal
+// access and a plain one to the same address there as one plain access, for
 // whichever accesses it happens to merge.  An empty volatile asm statement
 // (it emits nothing) at each end of a nontemporal group keeps them apart.
 template <int KIND, int DT, int OP, int PMAX, int U, bool WT>

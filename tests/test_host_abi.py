@@ -310,3 +310,18 @@ def test_bench_refuses_more_than_one_gpu():
                         "--warmup", "0"], capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_traffic_summary_follows_the_code_not_its_comments():
+    """The bench line reports the committed HBM-traffic figure only while the
+    collective sources still hash to the value the counters were taken on; a
+    comment edit keeps that hash and a code edit changes it."""
+    import bench
+
+    src = "int f(int x) {  // twice\n  return 2 * x; /* doubled */\n}\n"
+    recommented = "int f(int x) {  // two times x\n  return 2 * x;\n}\n"
+    edited = "int f(int x) {  // twice\n  return 3 * x; /* doubled */\n}\n"
+    assert bench.code_only(src) == bench.code_only(recommented)
+    assert bench.code_only(src) != bench.code_only(edited)
+    # the committed summary matches the sources in this tree
+    assert bench.read_traffic(4294967296) is not None
