@@ -18,6 +18,11 @@ Workloads (seed 0, numpy PCG64, rank r = r-th draw):
          tail) and 256 MiB per rank, bf16 and fp32     -> bit-equal to the
                                                           register-direct
                                                           kernel + samples
+  rules  the all-reduce's default launch inside each branch of its size- and
+         P-dependent rules (P = 2-16, 16-512 MiB per rank) -> oracle samples
+                                                             + replica identity
+  AG-wt  all-gather at P = 13 and 16, 256 MiB of input in all (write-through
+         by default)                                   -> exact slot checks
 The 1 GiB points draw their inputs on the GPU (PyTorch's seeded generator) and
 copy back only the sampled inputs for the oracle.
 """
@@ -252,3 +257,45 @@ def test_lds_pipeline_sweep_chunks(nbytes, dtype, chunk, stages):
         got = gather_at([outs[P - 1]], idx, dtype)[0]
         assert_parity(got, want, dtype, op, f"LDS S={stages} chunk={chunk} {dtype} {op}")
         del ref, outs
+
+
+# Every branch of the all-reduce's size- and P-dependent launch rules, at a
+# size where the branch applies, through the default launch (no config):
+# (P, MiB per rank, dtype, op, branch)
+RULE_CASES = [
+    (2, 192, "bf16", "sum", "P = 2, 129-256 MiB: unroll 1"),
+    (2, 320, "bf16", "max", "P = 2 above 256 MiB: write-through"),
+    (3, 64, "f32", "min", "3 <= P <= 8 up to 128 MiB: 8 KiB chunks, unroll 2"),
+    (5, 128, "bf16", "sum", "the same at its upper bound"),
+    (7, 160, "bf16", "sum", "P = 7 above 128 MiB: write-through"),
+    (8, 136, "bf16", "min", "P = 8 above 128 MiB: write-through"),
+    (9, 16, "f32", "sum", "P >= 9 from 16 MiB: write-through"),
+    (12, 32, "bf16", "max", "the same at P = 12"),
+    (16, 64, "bf16", "sum", "the same at P = 16"),
+    (6, 512, "bf16", "sum", "congruent inputs from 512 MiB: 16 KiB chunks, write-through"),
+]
+
+
+@pytest.mark.parametrize("P, mib, dtype, op, branch", RULE_CASES,
+                         ids=[f"P{c[0]}-{c[1]}MiB-{c[2]}-{c[3]}" for c in RULE_CASES])
+def test_ar_default_rule_branches(P, mib, dtype, op, branch):
+    esz = 4 if dtype == "f32" else 2
+    n = (mib << 20) // esz
+    print(f"AR default launch, P={P}, {mib} MiB per rank, {dtype} {op}: {branch}", flush=True)
+    dx = si.device_rank_buffers(P, n, dtype, "uniform", seed=P, device=DEV)
+    _ar_sampled(dx, P, n, dtype, op)
+
+
+@pytest.mark.parametrize("P", [13, 16])
+def test_ag_write_through_up_to_p16(P):
+    """All-gather at P = 13 and 16 with 256 MiB of input in all (write-through
+    by default): every output slot equals its owner's input, byte for byte."""
+    M = (256 << 20) // P // 2 // 128 * 128
+    print(f"AG default launch, P={P}, M={M} bf16", flush=True)
+    dx = si.device_rank_buffers(P, M, "bf16", "normal", seed=P, device=DEV)
+    dy = [torch.empty(P * M, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
+    ccl.check(ccl.ccl_all_gather(dx, dy, P, M, ccl.CCL_BFLOAT16, torch.cuda.current_stream()))
+    torch.cuda.synchronize()
+    for q in range(P):
+        for s in range(P):
+            assert torch.equal(dy[q][s * M:(s + 1) * M].view(torch.int16), dx[s].view(torch.int16)), (q, s)
