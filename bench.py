@@ -844,7 +844,8 @@ def defaults(dev, stream) -> None:
          turn): store policies by P and input size;
       D  all-reduce + RMSNorm, 2 GiB of input: the split-row form against
          the one-pass forms by P and row length;
-      E  reshard copy by replica count: chunk bytes, residency, cache hints.
+      E  reshard copy by replica count: chunk bytes, residency, cache hints,
+         store policy.
     """
     import numpy as np
     import torch
@@ -992,7 +993,8 @@ def defaults(dev, stream) -> None:
               ("32K <=2 nt st", L(chunk_bytes=32768, occupancy=2, nontemporal=2)),
               ("32K <=2 nt ld+st", L(chunk_bytes=32768, occupancy=2, nontemporal=3)),
               ("16K <=4 nt st", L(chunk_bytes=16384, occupancy=4, nontemporal=2)),
-              ("64K <=2 nt st", L(chunk_bytes=65536, occupancy=2, nontemporal=2))]
+              ("64K <=2 nt st", L(chunk_bytes=65536, occupancy=2, nontemporal=2)),
+              ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
     row = table("E. reshard copy bf16: layout x replicas per destination shard",
                 ["layout", "replicas"] + [k for k, _ in shapes])
     for name, shape, src, dst, rho in [
@@ -1001,7 +1003,11 @@ def defaults(dev, stream) -> None:
             ("MoE [64, 2048, 1408]", (64, 2048, 1408), ([8], 0, [("S", 0)]),
              ([4], 8, [("S", 1)]), 1),
             ("weight [8192, 28672] x 4 replicas", (8192, 28672), ([4], 0, [("S", 0)]),
-             ([4, 2], 4, ["R", ("S", 0)]), 4)]:
+             ([4, 2], 4, ["R", ("S", 0)]), 4),
+            ("weight [8192, 28672] x 8 replicas", (8192, 28672), ([4], 0, [("S", 0)]),
+             ([8, 2], 4, ["R", ("S", 0)]), 8),
+            ("MoE [64, 2048, 1408] x 4 replicas", (64, 2048, 1408), ([8], 0, [("S", 0)]),
+             ([4, 2], 8, ["R", ("S", 1)]), 4)]:
         st, plan = ccl.ccl_reshard_plan(ccl.make_tensor_desc(shape, ccl.CCL_BFLOAT16),
                                         ccl.make_mesh(src[0], src[1]), ccl.make_placements(src[2]),
                                         ccl.make_mesh(dst[0], dst[1]), ccl.make_placements(dst[2]))

@@ -184,6 +184,7 @@ struct ccl_plan {
   std::vector<std::vector<int32_t>> replicas;  // per dst shard: local dst indices, ascending
   std::vector<ccl::PlanInterval> intervals;
   bool offsets_aligned16 = true;         // every interval offset is a multiple of 16
+  bool dst_offsets_aligned256 = true;    // every interval's destination offset is a multiple of 256
   bool fp8_blocks_ok = true;             // every 128-element destination block lies in one interval
   // Device-side state, created on first use.
   std::mutex mu;

@@ -217,6 +217,7 @@ ccl_status_t ccl_reshard_plan(const ccl_tensor_desc_t *tensor, const ccl_mesh_t 
   const uint64_t block_bytes = 128 * (uint64_t)esz;
   for (const auto &iv : p->intervals) {
     if (iv.src_off % 16 || iv.dst_off % 16) p->offsets_aligned16 = false;
+    if (iv.dst_off % 256) p->dst_offsets_aligned256 = false;
     const uint64_t end = iv.dst_off + iv.len;
     const uint64_t local = p->dst_local_bytes[p->replicas[iv.dst_shard][0]];
     if (iv.dst_off % block_bytes || (end % block_bytes && end != local)) p->fp8_blocks_ok = false;

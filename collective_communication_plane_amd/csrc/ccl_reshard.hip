@@ -461,8 +461,8 @@ ccl_status_t reshard_launch(ccl_plan *p, const void *const *src, void *const *ds
   grid = std::min<uint64_t>(std::min<uint64_t>(grid, a.total_chunks), 1u << 30);
   const size_t lds = occupancy_lds(l.occupancy, 0);
   const dim3 g((unsigned)grid), b(kThreads);
-  // write-through stores take 31-bit offsets from the chunk's base
-  // (by default nontemporal only: write-through measured neutral, +-0.2 %)
+  // write-through stores take 31-bit offsets from the chunk's base (chosen by
+  // default at four or more replicas, see ccl_reshard_copy)
   const int sp = !l.nt_store ? ST_PLAIN
                  : (l.store_pol_set && l.store_wt && l.chunk_bytes <= (uint64_t(1) << 30)) ? ST_WT
                                                                                           : ST_NT;

@@ -104,7 +104,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   reshard copy    unroll 4; one replica per destination shard: 16 KiB
  *                   chunks, <= 4 WGs per CU, nontemporal loads and stores;
  *                   two or more: 32 KiB chunks, <= 2 WGs per CU,
- *                   nontemporal stores only
+ *                   nontemporal stores only (four or more: written through,
+ *                   see store_policy)
  *   reshard + fp8   32 KiB chunks, unroll 2, no cap (the quantizing pass does
  *                   enough ALU work per byte that it needs every resident wave)
  *   all-reduce + RMSNorm  P >= 8 with rows of at least 8 KiB per rank:
@@ -182,13 +183,15 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                all-gather and broadcast at P = 2, at 7 <= P <= 16 with at
  *                most 256 MiB of input in all and at 4 <= P <= 6 with at most
  *                64 MiB (from P = 9 on with <= 4 WGs per CU instead of 3),
- *                each only where every
+ *                for the reshard copy with four or more replicas per
+ *                destination shard, each only where every
  *                output's stores start on a 256-byte boundary (partial lines
  *                written through cost far more than they save); nontemporal
  *                only for the other all-reduces, the other all-gathers and
- *                broadcasts, the reshard copy, the FP8 reshard and the fused
- *                RMSNorm's one-pass forms (within +-1.3 % of write-through,
- *                either sign); the split-row RMSNorm as stated above.
+ *                broadcasts, the other reshard copies, the FP8 reshard and
+ *                the fused RMSNorm's one-pass forms (within +-1.3 % of
+ *                write-through, either sign); the split-row RMSNorm as
+ *                stated above.
  *                Write-through applies to the register-direct kernels only
  *                (not the LDS pipeline or the realigning kernel).  It needs
  *                >= 4 resident workgroups per CU to cover its longer store

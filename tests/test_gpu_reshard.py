@@ -184,6 +184,34 @@ def test_reshard_rw_a_full_size():
     _sample_check(shape, src, dst, src_host, ddst)
 
 
+@pytest.mark.parametrize("rho", [4, 8])
+def test_reshard_replicated_full_size(rho):
+    """The weight of the first full-size case sent to rho replicas of each of
+    two row shards ([rho, 2] mesh, Replicate x Shard(0)): with four or more
+    replicas and 256-byte aligned destinations the stores write through by
+    default."""
+    shape = (8192, 28672)
+    src = ([4], 0, [("S", 0)])
+    dst = ([rho, 2], 4, ["R", ("S", 0)])
+    print(f"reshard {shape} -> {rho} replicas x 2 shards", flush=True)
+    G = si.tensor(shape, "bf16", "w002", seed=rho)
+    src_host = local_blocks(G, src)
+    del G
+    dsrc = [torch.from_numpy(b.view(np.uint8)).to(DEV) for b in src_host]
+    ddst = [torch.empty(4096 * 28672 * 2, dtype=torch.uint8, device=DEV) for _ in range(2 * rho)]
+    plan = make_plan(shape, ccl.CCL_BFLOAT16, src, dst)
+    try:
+        ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, torch.cuda.current_stream()))
+        torch.cuda.synchronize()
+    finally:
+        ccl.check(ccl.ccl_plan_destroy(plan))
+    # destination rank l holds row block l % 2: source ranks 2t and 2t+1 back to back
+    for l in range(2 * rho):
+        t = l % 2
+        assert torch.equal(ddst[l], torch.cat([dsrc[2 * t], dsrc[2 * t + 1]])), l
+    _sample_check(shape, src, dst, src_host, ddst[:4])
+
+
 def test_reshard_rw_b_full_size():
     shape = (64, 2048, 1408)
     src = ([8], 0, [("S", 0)])
