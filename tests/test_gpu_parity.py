@@ -168,6 +168,24 @@ def test_launch_config_does_not_change_results(cfg):
         np.testing.assert_array_equal(got[q], np.concatenate(xg))
 
 
+@pytest.mark.parametrize("P", [2, 3, 4, 5, 6, 7, 9, 12, 16])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unroll2_all_reduce_folds_in_rank_order(P, dtype):
+    """With two vectors per lane in flight and nontemporal stores, the
+    all-reduce kernel loads the last rank into its first slot and puts the
+    slots back in rank order before the fold; a fold in any other order would
+    still land within the parity bar, so the result must be bit-equal.  With
+    these fp32 normal draws, starting the fold at rank P - 1 instead changes
+    16,000-33,000 of the 50,001 sums at every P from 3 (two-term sums are
+    order-free)."""
+    n = 50001
+    xs = si.rank_buffers(P, n, dtype, "normal", seed=40 + P)
+    want = oracle.all_reduce(xs, dtype, "sum")
+    got = run_ar(xs, dtype, "sum", cfg=ccl.LaunchConfig(unroll=2, store_policy=2))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want[q])
+
+
 # -------------------------------------------------------- reduce-scatter
 
 def run_rs(xs, dtype, op, offset=0, cfg=None, out_offset=None):
