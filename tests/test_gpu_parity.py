@@ -157,6 +157,12 @@ def test_launch_config_does_not_change_results(cfg):
     got = run_ar(xs, "bf16", "sum", cfg=ccl.LaunchConfig(**cfg))
     for q in range(P):
         np.testing.assert_array_equal(got[q], want[q])
+    # fp32 normal draws, whose sums change bits under any other fold order
+    xf = si.rank_buffers(P, n, "f32", "normal", seed=8)
+    want = oracle.all_reduce(xf, "f32", "sum")
+    got = run_ar(xf, "f32", "sum", cfg=ccl.LaunchConfig(**cfg))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q].view(np.uint32), want[q].view(np.uint32))
     # reduce-scatter and all-gather under the same config
     m = n // P + 3
     xr = si.rank_buffers(P, P * m, "f32", "uniform", seed=6)
@@ -507,6 +513,29 @@ def test_outputs_misaligned_to_each_other_use_elementwise_kernel():
     got = run_offsets("ag", xg, "bf16", "sum", [2, 0, 6, 4], [0, 2, 4, 8])
     for q in range(P):
         np.testing.assert_array_equal(got[q], np.concatenate(xg))
+
+
+@pytest.mark.parametrize("in_offs, out_offs, path", [
+    ([4] * 6, [4] * 6, "scalar head and tail around the vector body"),
+    ([0] * 6, [4] * 6, "inputs realigned in VGPRs"),
+    ([0, 4, 8, 12, 0, 4], [8] * 6, "inputs at assorted offsets, realigned"),
+    ([0] * 6, [0, 4, 8, 12, 0, 4], "outputs misaligned to each other: element-wise kernel"),
+])
+def test_misaligned_paths_fold_in_rank_order(in_offs, out_offs, path):
+    """Every kernel family folds in rank order: fp32 normal sums, whose bits
+    change under any other order, equal the oracle's bit for bit on the paths
+    that misaligned buffers take (all-reduce and reduce-scatter)."""
+    P = 6
+    xs = si.rank_buffers(P, 30011, "f32", "normal", seed=51)
+    got = run_offsets("ar", xs, "f32", "sum", in_offs, out_offs)
+    want = oracle.all_reduce(xs, "f32", "sum")
+    for q in range(P):
+        np.testing.assert_array_equal(got[q].view(np.uint32), want[q].view(np.uint32), path)
+    xr = si.rank_buffers(P, P * 5003, "f32", "normal", seed=52)
+    got = run_offsets("rs", xr, "f32", "sum", in_offs, out_offs)
+    want = oracle.reduce_scatter(xr, "f32", "sum")
+    for s_ in range(P):
+        np.testing.assert_array_equal(got[s_].view(np.uint32), want[s_].view(np.uint32), path)
 
 
 @pytest.mark.parametrize("P", [1, 2, 3, 4, 6, 8, 12, 16])
