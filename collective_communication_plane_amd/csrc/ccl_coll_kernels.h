@@ -383,10 +383,17 @@ __global__ void __launch_bounds__(kThreads) coll_realign_kernel(CollArgs a) {
       u32x4 y;
       if constexpr (KIND == KIND_AG) y = x[0];
       else y = fold_vec<DT, OP, NI>(x, ni);
+      // Every store nontemporal: the loads above already go through the
+      // cache, and a cacheable output on top of them measured slower.  Fenced
+      // as in coll_vec_kernel, without which the compiler merged one output's
+      // store into the plain path's (all-gather 9-11 % slower, reduce-scatter
+      // 4-5 %).
       if (nts) {
+        asm volatile("");
 #pragma unroll
         for (int q = 0; q < NO; ++q)
           if (q < no) st_nt(ob[q] + v * kVecBytes, y);
+        asm volatile("");
       } else {
 #pragma unroll
         for (int q = 0; q < NO; ++q)
@@ -601,13 +608,25 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
         u32x4 y;
         if constexpr (KIND == KIND_AG) y = x[0];
         else y = fold_vec<DT, OP, NI>(x, ni);
+        // The inputs arrive through nontemporal loads; output 0's stores stay
+        // cacheable (the host puts the all-reduce's last output there), the
+        // reduce-scatter's single output does not.  The groups are fenced as
+        // in coll_vec_kernel: a per-store choice between the two hints was
+        // merged by the compiler into plain stores to every output (10-15 %
+        // slower for the all-reduce, 4-5 % for the all-gather).
+        constexpr bool pout0 = KIND != KIND_RS;
+        if (nts) {
+          asm volatile("");
 #pragma unroll
-        for (int q = 0; q < NO; ++q)
-          if (q < no) {
-            char *d = out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes;
-            if (nts) st_nt(d, y);
-            else st_plain(d, y);
-          }
+          for (int q = pout0 ? 1 : 0; q < NO; ++q)
+            if (q < no) st_nt(out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes, y);
+          asm volatile("");
+          if constexpr (pout0) st_plain(out_at<KIND>(a, s, 0, head, esz) + vv * kVecBytes, y);
+        } else {
+#pragma unroll
+          for (int q = 0; q < NO; ++q)
+            if (q < no) st_plain(out_at<KIND>(a, s, q, head, esz) + vv * kVecBytes, y);
+        }
       }
       cursor_next(a, k);
     }

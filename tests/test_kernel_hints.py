@@ -1,6 +1,6 @@
-"""The register-direct collective kernels' cache hints, read from the gfx950
-assembly that hipcc emits for them (code built here, from this repository's
-sources).
+"""The collective kernels' cache hints (register-direct, and the stores of the
+LDS pipeline and the realigning kernel), read from the gfx950 assembly that
+hipcc emits for them (code built here, from this repository's sources).
 
 Each stream of the register-direct kernel is meant to be nontemporal except
 one (input 0's loads or output 0's stores, by collective), and a launch that
@@ -114,3 +114,27 @@ def test_loads_of_a_lane_are_all_in_flight_before_the_fold(asm):
     assert len(idx) == 8
     between = lines[idx[0]:idx[-1]]
     assert not any(l.startswith("s_waitcnt") and "vmcnt" in l for l in between)
+
+
+# The LDS pipeline and the realigning kernel, P <= 8: (slice, kernel symbol
+# stem, nontemporal stores, plain stores).  LDS pipeline: output 0 cacheable
+# for the all-reduce and all-gather (7 hinted stores and one plain, plus the
+# all-plain path's 8), the reduce-scatter's one output hinted.  Realigning
+# kernel: every store hinted (its loads go through the cache).
+OTHER_CASES = [
+    ("ar_bf16", "15coll_lds_kernelILi0ELi1ELi0ELi8ELi2E", 7, 9),
+    ("rs_bf16", "15coll_lds_kernelILi1ELi1ELi0ELi8ELi2E", 1, 1),
+    ("ag_b16", "15coll_lds_kernelILi2ELi1ELi0ELi8ELi2E", 7, 9),
+    ("ar_bf16", "19coll_realign_kernelILi0ELi1ELi0ELi8E", 8, 8),
+    ("rs_bf16", "19coll_realign_kernelILi1ELi1ELi0ELi8E", 1, 1),
+    ("ag_b16", "19coll_realign_kernelILi2ELi1ELi0ELi8E", 8, 8),
+]
+
+
+@pytest.mark.parametrize("slice_, stem, st_nt, st_plain", OTHER_CASES)
+def test_lds_and_realign_store_hints(asm, slice_, stem, st_nt, st_plain):
+    sym = f"_ZN3ccl12_GLOBAL__N_1{stem}EEvNS_8CollArgsE"
+    m = re.search(rf"^{re.escape(sym)}:.*?^\s*s_endpgm", asm[slice_], re.S | re.M)
+    assert m, sym
+    got = counts(m.group(0))
+    assert (got["st_nt"], got["st_plain"]) == (st_nt, st_plain), got
