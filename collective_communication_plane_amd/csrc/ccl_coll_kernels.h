@@ -46,8 +46,8 @@ struct CollArgs {
   uint64_t total_chunks;
   int P;
   // bit 0: nontemporal loads, bit 1: nontemporal stores, bit 2: those stores
-  // write-through (register-direct kernel only; the host sets it only for
-  // chunks of at most 1 GiB)
+  // write-through (register-direct kernel and LDS pipeline; the host sets it
+  // only for chunks of at most 1 GiB)
   int flags;
 };
 
@@ -520,7 +520,7 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
   const int P = a.P;
   const int ni = KIND == KIND_AG ? 1 : P;
   const int no = KIND == KIND_RS ? 1 : P;
-  const bool ntl = a.flags & 1, nts = a.flags & 2;
+  const bool ntl = a.flags & 1, nts = a.flags & 2, wts = a.flags & 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
 
@@ -536,7 +536,19 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
       uint64_t vv = k.v0 + k.t * kTileVecs + (uint64_t)p * 64 + lane;
       if (vv >= k.v1) vv = k.v1 - 1;
       char *dst = lds + stage * kStageBytes + p * 64 * kVecBytes;
-      if (ntl) {
+      if (ntl && wts) {
+        // with write-through stores input 0's loads stay cacheable, as in
+        // coll_vec_kernel (the one cacheable stream of the call)
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(in_at<KIND>(a, k.s, 0, head, esz) + vv * kVecBytes),
+            (__attribute__((address_space(3))) void *)(dst), kVecBytes, 0, 0);
+#pragma unroll
+        for (int r = 1; r < NI; ++r)
+          if (r < ni)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(in_at<KIND>(a, k.s, r, head, esz) + vv * kVecBytes),
+                (__attribute__((address_space(3))) void *)(dst + r * kTileBytes), kVecBytes, 0, 2);
+      } else if (ntl) {
 #pragma unroll
         for (int r = 0; r < NI; ++r)
           if (r < ni)
@@ -615,7 +627,16 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
         // merged by the compiler into plain stores to every output (10-15 %
         // slower for the all-reduce, 4-5 % for the all-gather).
         constexpr bool pout0 = KIND != KIND_RS;
-        if (nts) {
+        if (wts) {
+          // write-through, from the wave's base in this tile (kept in scalar
+          // registers, see st_wt)
+          const uint64_t vbase = k.v0 + k.t * kTileVecs + (uint64_t)w * 64;
+#pragma unroll
+          for (int q = 0; q < NO; ++q)
+            if (q < no)
+              st_wt(wave_uniform(out_at<KIND>(a, s, q, head, esz) + vbase * kVecBytes),
+                    (uint64_t)lane * kVecBytes, y);
+        } else if (nts) {
           asm volatile("");
 #pragma unroll
           for (int q = pout0 ? 1 : 0; q < NO; ++q)

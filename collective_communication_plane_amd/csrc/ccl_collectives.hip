@@ -147,7 +147,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
     if (!l.occupancy_set) occupancy = d.kind != KIND_AG ? (many ? 4 : 8) : d.P <= 6 ? 4 : 3;
     if (!l.nt_set && d.kind == KIND_RS) a.flags &= ~1;
   }
-  // Write-through stores (register-direct kernel only), by default where they
+  // Write-through stores (register-direct kernel and LDS pipeline), by default where they
   // won in same-binary A/B runs on MI355X (bf16, separate kernel
   // instantiations): the reduce-scatter and reduce at P <= 8 (+3 % at P <= 4,
   // +1-8 % at P = 7, 8 from 64 to 512 MiB per rank; -0.4 to +0.8 % from
@@ -186,7 +186,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
              (d.P >= 4 && d.P <= 6 && ag_in_bytes <= (uint64_t(64) << 20)))
           : d.kind == KIND_RS ? d.P <= 8
                               : d.P >= 2 && per_rank >= ar_wt_from);
-  wt = wt && l.nt_store && !realign && l.stages <= 1 && chunk_bytes <= (uint64_t(1) << 30);
+  wt = wt && l.nt_store && !realign && chunk_bytes <= (uint64_t(1) << 30);
   if (wt) a.flags |= 4;
   if (wt && d.kind == KIND_AG && d.P >= 9 && !l.occupancy_set) occupancy = 4;
   if (wt && d.kind == KIND_AR && d.P <= 4) {

@@ -139,8 +139,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *   workgroups   grid size; chunks are dealt to workgroups round-robin.
  *                Default: one workgroup per chunk.
  *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS
- *                pipeline (never chosen by default: on MI355X it trails the
- *                register-direct kernel on every workload measured):
+ *                pipeline (never chosen by default: on MI355X it is level
+ *                with the register-direct kernel on the all-reduce at
+ *                192 MiB-1 GiB per rank and behind it elsewhere):
  *                producer waves stream tiles into a ring of
  *                `stages` LDS buffers with asynchronous global->LDS loads,
  *                consumer waves fold and store them (clamped so the ring
@@ -192,8 +193,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                the fused RMSNorm's one-pass forms (within +-1.3 % of
  *                write-through, either sign); the split-row RMSNorm as
  *                stated above.
- *                Write-through applies to the register-direct kernels only
- *                (not the LDS pipeline or the realigning kernel).  It needs
+ *                Write-through applies to the register-direct kernels and
+ *                the LDS pipeline (not the realigning kernel); with it both
+ *                keep input 0's loads cacheable.  It needs
  *                >= 4 resident workgroups per CU to cover its longer store
  *                completion in the all-gather; with fewer it can be much
  *                slower.  Ignored when nontemporal stores are off.

@@ -1,6 +1,7 @@
-"""The collective kernels' cache hints (register-direct, and the stores of the
-LDS pipeline and the realigning kernel), read from the gfx950 assembly that
-hipcc emits for them (code built here, from this repository's sources).
+"""The collective kernels' cache hints (register-direct, the LDS pipeline's
+loads and stores, and the realigning kernel's stores), read from the gfx950
+assembly that hipcc emits for them (code built here, from this repository's
+sources).
 
 Each stream of the register-direct kernel is meant to be nontemporal except
 one (input 0's loads or output 0's stores, by collective), and a launch that
@@ -117,24 +118,35 @@ def test_loads_of_a_lane_are_all_in_flight_before_the_fold(asm):
 
 
 # The LDS pipeline and the realigning kernel, P <= 8: (slice, kernel symbol
-# stem, nontemporal stores, plain stores).  LDS pipeline: output 0 cacheable
-# for the all-reduce and all-gather (7 hinted stores and one plain, plus the
-# all-plain path's 8), the reduce-scatter's one output hinted.  Realigning
-# kernel: every store hinted (its loads go through the cache).
+# stem, nontemporal stores, plain stores, written-through stores, hinted and
+# plain direct-to-LDS loads).  LDS pipeline: output 0 cacheable for the
+# all-reduce and all-gather (7 hinted stores and one plain, plus the all-plain
+# path's 8), the reduce-scatter's one output hinted; its write-through path
+# writes every output through.  Its producer issues the rank loads of a tile
+# in three forms (all plain, all hinted, and the write-through path's input 0
+# plain with the rest hinted), each twice (the pipeline's fill and its steady
+# state): 8 + 8 + 8 per form for P = 8, 30 of the 48 hinted.  The
+# all-gather's one input gives 2 + 2 + 2, the hinted path's 2 hinted.
+# Realigning kernel: every store hinted (its loads go through the cache).
 OTHER_CASES = [
-    ("ar_bf16", "15coll_lds_kernelILi0ELi1ELi0ELi8ELi2E", 7, 9),
-    ("rs_bf16", "15coll_lds_kernelILi1ELi1ELi0ELi8ELi2E", 1, 1),
-    ("ag_b16", "15coll_lds_kernelILi2ELi1ELi0ELi8ELi2E", 7, 9),
-    ("ar_bf16", "19coll_realign_kernelILi0ELi1ELi0ELi8E", 8, 8),
-    ("rs_bf16", "19coll_realign_kernelILi1ELi1ELi0ELi8E", 1, 1),
-    ("ag_b16", "19coll_realign_kernelILi2ELi1ELi0ELi8E", 8, 8),
+    ("ar_bf16", "15coll_lds_kernelILi0ELi1ELi0ELi8ELi2E", 7, 9, 8, 30, 18),
+    ("rs_bf16", "15coll_lds_kernelILi1ELi1ELi0ELi8ELi2E", 1, 1, 1, 30, 18),
+    ("ag_b16", "15coll_lds_kernelILi2ELi1ELi0ELi8ELi2E", 7, 9, 8, 2, 4),
+    ("ar_bf16", "19coll_realign_kernelILi0ELi1ELi0ELi8E", 8, 8, 0, 0, 0),
+    ("rs_bf16", "19coll_realign_kernelILi1ELi1ELi0ELi8E", 1, 1, 0, 0, 0),
+    ("ag_b16", "19coll_realign_kernelILi2ELi1ELi0ELi8E", 8, 8, 0, 0, 0),
 ]
 
 
-@pytest.mark.parametrize("slice_, stem, st_nt, st_plain", OTHER_CASES)
-def test_lds_and_realign_store_hints(asm, slice_, stem, st_nt, st_plain):
+@pytest.mark.parametrize("slice_, stem, st_nt, st_plain, st_wt, lds_nt, lds_plain", OTHER_CASES)
+def test_lds_and_realign_hints(asm, slice_, stem, st_nt, st_plain, st_wt, lds_nt, lds_plain):
     sym = f"_ZN3ccl12_GLOBAL__N_1{stem}EEvNS_8CollArgsE"
     m = re.search(rf"^{re.escape(sym)}:.*?^\s*s_endpgm", asm[slice_], re.S | re.M)
     assert m, sym
-    got = counts(m.group(0))
-    assert (got["st_nt"], got["st_plain"]) == (st_nt, st_plain), got
+    body = m.group(0)
+    got = counts(body)
+    lines = body.splitlines()
+    got_lds_nt = sum(1 for l in lines if re.search(r"global_load_lds_dwordx4 .* nt\s*$", l))
+    got_lds_plain = sum(1 for l in lines if re.search(r"global_load_lds_dwordx4 .* off\s*$", l))
+    assert (got["st_nt"], got["st_plain"], got["st_wt"], got_lds_nt, got_lds_plain) == \
+        (st_nt, st_plain, st_wt, lds_nt, lds_plain), (got, got_lds_nt, got_lds_plain)
