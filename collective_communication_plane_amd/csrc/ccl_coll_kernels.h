@@ -620,16 +620,19 @@ __global__ void __launch_bounds__(kLdsThreads) coll_lds_kernel(CollArgs a) {
         u32x4 y;
         if constexpr (KIND == KIND_AG) y = x[0];
         else y = fold_vec<DT, OP, NI>(x, ni);
-        // The inputs arrive through nontemporal loads; output 0's stores stay
-        // cacheable (the host puts the all-reduce's last output there), the
-        // reduce-scatter's single output does not.  The groups are fenced as
-        // in coll_vec_kernel: a per-store choice between the two hints was
+        // One cacheable stream per call, as in coll_vec_kernel.  Writing
+        // through, that is input 0's loads (producer above) and every output
+        // is written through.  Otherwise the inputs arrive through
+        // nontemporal loads and output 0's stores stay cacheable (the host
+        // puts the all-reduce's last output there); the reduce-scatter's
+        // single output does not.  The nontemporal group is fenced as in
+        // coll_vec_kernel: a per-store choice between the two hints was
         // merged by the compiler into plain stores to every output (10-15 %
         // slower for the all-reduce, 4-5 % for the all-gather).
         constexpr bool pout0 = KIND != KIND_RS;
         if (wts) {
-          // write-through, from the wave's base in this tile (kept in scalar
-          // registers, see st_wt)
+          // from the wave's base in this tile, kept in scalar registers (see
+          // st_wt)
           const uint64_t vbase = k.v0 + k.t * kTileVecs + (uint64_t)w * 64;
 #pragma unroll
           for (int q = 0; q < NO; ++q)
