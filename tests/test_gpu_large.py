@@ -144,14 +144,14 @@ def test_all_reduce_rmsnorm_past_4gib_per_rank():
 
 
 @pytest.mark.parametrize("P", [7, 8, 12])
-def test_reduce_scatter_and_reduce_across_the_lds_size_rule(P):
-    """At P = 7, 8 reduce-scatter and reduce switch from the register-direct
-    kernel to the LDS pipeline past 160 MiB per rank when write-through stores
-    do not apply (P = 12 stays register-direct with its own defaults).  These
-    torch tensors start on 256 bytes, so the defaults stay register-direct with
-    write-through stores; the LDS pipeline runs as the forced launch
-    (stages = 2) and the nontemporal-only one as store_policy = 2.  Every form
-    on both sides of that size must give the oracle's values (sum, sampled)."""
+def test_reduce_scatter_and_reduce_launch_forms_around_160mib(P):
+    """Reduce-scatter and reduce at P = 7, 8, 12 on both sides of 160 MiB per
+    rank, where the LDS pipeline once took over from the register-direct
+    kernel.  These torch tensors start on 256 bytes, so the default launch is
+    register-direct with write-through stores at P <= 8.  It, the LDS pipeline
+    forced with stages = 2 (writing through as the default would) and
+    nontemporal-only stores (store_policy = 2) must all give the oracle's
+    values (sum, sampled) and equal one another."""
     TORCH = {"bf16": torch.int16, "f32": torch.int32}
     for dtype, per_rank_mib in (("bf16", 144), ("bf16", 176), ("f32", 168)):
         esz = 2 if dtype == "bf16" else 4
