@@ -50,8 +50,9 @@ Other modes:
                 forms (buffer sets used in turn); one JSON line each.
   --streams     all-reduce bandwidth against the number of ranks P = 1, 2, 4, 8,
                 16 at a fixed 2 GiB of input (P = 1 is a plain copy through the
-                same kernel), with the default and an uncapped occupancy, next
-                to a plain 1 GiB device copy; one JSON line per point.
+                same kernel), with the defaults, an uncapped occupancy and each
+                store policy forced, next to a plain 1 GiB device copy; one
+                JSON line per point.
 """
 from __future__ import annotations
 
@@ -652,7 +653,10 @@ def placements(dev, stream, layout: str, steps: int) -> None:
 
 
 def streams(dev, stream) -> None:
-    """All-reduce GB/s against P at a fixed total size (2 GiB in, 2 GiB out)."""
+    """All-reduce GB/s against P at a fixed total size (2 GiB in, 2 GiB out),
+    one tensor per rank: library defaults, no residency cap, and each store
+    policy forced (write-through, nontemporal only).  At P = 1 the call is a
+    copy through the library's own kernel."""
     import torch
 
     import synth_inputs as si
@@ -669,16 +673,16 @@ def streams(dev, stream) -> None:
         n = (1 << 30) // P  # bf16 elements per rank: 2 GiB of input in total
         dx = si.device_rank_buffers(P, n, "bf16", "uniform", seed=0, device=dev)
         dy = [torch.empty_like(t) for t in dx]
-        for occ in (0, 32):
-            cfg = ccl.LaunchConfig(occupancy=occ) if occ else None
+        for label, cfg in (("default", None), ("uncapped", ccl.LaunchConfig(occupancy=32)),
+                           ("write_through", ccl.LaunchConfig(store_policy=1)),
+                           ("nontemporal", ccl.LaunchConfig(store_policy=2))):
             ms = timed(lambda: ccl.check(ccl.ccl_all_reduce(dx, dy, P, n, ccl.CCL_BFLOAT16,
                                                             ccl.CCL_SUM, stream, cfg)),
                        20, 3, stream, 0.2)
             gbs = 2 * P * n * 2 / (ms * 1e-3) / 1e9
-            print(json.dumps({"streams": f"all_reduce_P{P}",
-                              "occupancy": occ or "default", "ms": round(ms, 5),
-                              "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}),
-                  flush=True)
+            print(json.dumps({"streams": f"all_reduce_P{P}", "launch": label,
+                              "ms": round(ms, 5), "GB/s": round(gbs, 1),
+                              "frac": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
         del dx, dy
         torch.cuda.empty_cache()
 

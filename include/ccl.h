@@ -82,8 +82,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  * re-measure every rule below against its alternatives):
  *   all-reduce      P = 1: 8 KiB chunks, unroll 1, <= 8 WGs per CU;
  *                   P = 2: 8 KiB chunks, unroll 2 (unroll 1 above 128 and
- *                   up to 256 MiB per rank), <= 8 WGs per CU (<= 3 with
- *                   write-through stores);
+ *                   up to 256 MiB per rank), <= 8 WGs per CU; with
+ *                   write-through stores 4 KiB chunks, unroll 1, <= 6 WGs
+ *                   per CU;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
  *                   write-through stores: 8 KiB chunks, <= 3 WGs per CU);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but

@@ -264,7 +264,8 @@ def test_lds_pipeline_sweep_chunks(nbytes, dtype, chunk, stages):
 # (P, MiB per rank, dtype, op, branch)
 RULE_CASES = [
     (2, 192, "bf16", "sum", "P = 2, 129-256 MiB: unroll 1"),
-    (2, 320, "bf16", "max", "P = 2 above 256 MiB: write-through"),
+    (2, 320, "bf16", "max", "P = 2 above 256 MiB: write-through, 4 KiB chunks, unroll 1"),
+    (4, 256, "f32", "min", "P = 3, 4 from 256 MiB: write-through, 8 KiB chunks"),
     (3, 64, "f32", "min", "3 <= P <= 8 up to 128 MiB: 8 KiB chunks, unroll 2"),
     (5, 128, "bf16", "sum", "the same at its upper bound"),
     (7, 160, "bf16", "sum", "P = 7 above 128 MiB: write-through"),
