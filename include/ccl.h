@@ -141,8 +141,8 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                Default: one workgroup per chunk.
  *   stages       1 = register-direct (loads land in VGPRs), 2..4 = LDS
  *                pipeline (never chosen by default: on MI355X it is level
- *                with the register-direct kernel on the all-reduce at
- *                192 MiB-1 GiB per rank and behind it elsewhere):
+ *                with the register-direct kernel on the all-reduce and
+ *                behind it on the reduce-scatter and all-gather):
  *                producer waves stream tiles into a ring of
  *                `stages` LDS buffers with asynchronous global->LDS loads,
  *                consumer waves fold and store them (clamped so the ring
@@ -166,7 +166,11 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                last rank's output (with write-through stores the loads
  *                of the first input instead; with unroll 2 the loads of
  *                the last rank's input as well), for the other
- *                collectives the loads of the first input.
+ *                collectives the loads of the first input.  The LDS
+ *                pipeline does the same with write-through stores; with
+ *                nontemporal ones it keeps output 0's stores cacheable for
+ *                the all-reduce and all-gather and no stream for the
+ *                reduce-scatter.
  *   occupancy    at most this many workgroups resident per compute unit
  *                (enforced by reserving LDS), 1..32; 32 is effectively no
  *                cap.  Fewer resident waves keep fewer DRAM pages open at
