@@ -287,6 +287,36 @@ def test_ar_default_rule_branches(P, mib, dtype, op, branch):
     _ar_sampled(dx, P, n, dtype, op)
 
 
+@pytest.mark.parametrize("P, mib", [(2, 288), (4, 256), (8, 136)])
+def test_ar_write_through_shapes_with_a_ragged_tail(P, mib):
+    """The all-reduce's write-through shapes (P = 2: 4 KiB chunks, unroll 1;
+    P = 4: 8 KiB chunks; P = 8: 4 KiB chunks) on a count 5 elements past whole
+    vectors, so the last chunk is partial and a scalar tail follows it.  Every
+    output equals the nontemporal-only launch (store_policy = 2) byte for byte,
+    and sampled points, the last 4096 elements among them, equal the oracle."""
+    n = (mib << 20) // 2 + 5
+    print(f"AR write-through shape, P={P}, n={n} bf16", flush=True)
+    dx = si.device_rank_buffers(P, n, "bf16", "normal", seed=40 + P, device=DEV)
+    wt = [torch.empty_like(t) for t in dx]
+    nt = [torch.empty_like(t) for t in dx]
+    stream = torch.cuda.current_stream()
+    ccl.check(ccl.ccl_all_reduce(dx, wt, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream))
+    ccl.check(ccl.ccl_all_reduce(dx, nt, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream,
+                                 ccl.LaunchConfig(store_policy=2)))
+    torch.cuda.synchronize()
+    for q in range(P):
+        assert torch.equal(wt[q].view(torch.int16), nt[q].view(torch.int16)), q
+    idx = np.unique(np.concatenate([si.sample_indices(n, 50_000, seed=P),
+                                    np.arange(n - 4096, n, dtype=np.uint64)]))
+    xin = gather_at(dx, idx, "bf16")
+    want = oracle.fold_at(xin, "bf16", "sum", np.arange(idx.size, dtype=np.uint64))
+    for q in (0, P - 1):
+        got = gather_at([wt[q]], idx, "bf16")[0]
+        assert_parity(got, want, "bf16", "sum", f"AR WT P={P} rank {q}")
+    del dx, wt, nt
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("P", [13, 16])
 def test_ag_write_through_up_to_p16(P):
     """All-gather at P = 13 and 16 with 256 MiB of input in all (write-through
