@@ -883,6 +883,8 @@ def defaults(dev, stream) -> None:
               ("8K u2 <=4", L(chunk_bytes=8192, unroll=2, occupancy=4)),
               ("16K u1 <=3", L(chunk_bytes=16384, unroll=1, occupancy=3)),
               ("8K u1 <=8", L(chunk_bytes=8192, unroll=1, occupancy=8)),
+              ("8K u1 <=3", L(chunk_bytes=8192, unroll=1, occupancy=3)),
+              ("4K u1 <=6", L(chunk_bytes=4096, unroll=1, occupancy=6)),
               ("default + wt", L(store_policy=1)), ("default + nt", L(store_policy=2))]
     row = table("A. all-reduce bf16: P x MiB per rank x layout",
                 ["P", "MiB/rank", "layout"] + [k for k, _ in shapes])
