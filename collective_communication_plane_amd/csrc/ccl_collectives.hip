@@ -193,9 +193,10 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // layouts): P = 2 above 256 MiB per rank with 4 KiB chunks, unroll 1 and
   // <= 6 WGs per CU, +0.1-9 % over 8 KiB / unroll 2 / <= 3 in all 18 cells at
   // 288 MiB-1 GiB (<= 4, 5, 7, 8 or uncapped trail <= 6); P = 3, 4 with 8 KiB
-  // chunks and <= 3 WGs per CU (P = 4 at 256 MiB-1 GiB: the other shapes -0.2
-  // to -13 %).  P = 1 has write-through only when asked for and keeps its
-  // own shape (the <= 3 cap halves a copy's rate there).
+  // chunks and <= 3 WGs per CU (P = 4 at 256 MiB-1 GiB: the other shapes
+  // tried within 1.2 % of it or behind, by up to 13 %).  P = 1 has
+  // write-through only when asked for and keeps its own shape (the <= 3 cap
+  // halves a copy's rate there).
   if (wt && d.kind == KIND_AR && d.P == 2) {
     if (!l.chunk_set) chunk_bytes = 4096;
     if (!l.unroll_set) unroll = 1;
