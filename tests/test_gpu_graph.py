@@ -126,12 +126,16 @@ def test_fused_and_reshard_calls_in_a_graph():
 def test_write_through_calls_in_a_graph():
     """Write-through stores (buffer stores with the device-scope bit) replay
     bit-identically from a graph: the all-gather on line-aligned shards by
-    default, the split-row RMSNorm, the all-reduce, reshard copy and FP8
-    codes by request."""
+    default, the split-row RMSNorm, the all-reduce (register-direct at P = 8
+    and 2, and the LDS pipeline), reshard copy and FP8 codes by request."""
     P, n, m = 8, 65536, 8192
     wt = ccl.LaunchConfig(store_policy=1)
+    wt_lds = ccl.LaunchConfig(store_policy=1, stages=2, chunk_bytes=4096)
     x_ar = [torch.empty(n, dtype=torch.bfloat16, device=DEV) for _ in range(P)]
     y_ar = [torch.empty_like(t) for t in x_ar]
+    y_lds = [torch.empty_like(t) for t in x_ar]
+    x_2 = [torch.empty(n + 3, dtype=torch.float32, device=DEV) for _ in range(2)]
+    y_2 = [torch.empty_like(t) for t in x_2]
     x_ag = [torch.empty(m, dtype=torch.float32, device=DEV) for _ in range(P)]
     y_ag = [torch.empty(P * m, dtype=torch.float32, device=DEV) for _ in range(P)]
     rows, hidden = 9, 16384
@@ -150,14 +154,17 @@ def test_write_through_calls_in_a_graph():
     try:
         def calls(stream):
             ccl.check(ccl.ccl_all_reduce(x_ar, y_ar, P, n, ccl.CCL_BFLOAT16, ccl.CCL_SUM, stream, wt))
+            ccl.check(ccl.ccl_all_reduce(x_ar, y_lds, P, n, ccl.CCL_BFLOAT16, ccl.CCL_MIN, stream,
+                                         wt_lds))
+            ccl.check(ccl.ccl_all_reduce(x_2, y_2, 2, n + 3, ccl.CCL_FLOAT32, ccl.CCL_SUM, stream, wt))
             ccl.check(ccl.ccl_all_gather(x_ag, y_ag, P, m, ccl.CCL_FLOAT32, stream))
             ccl.check(ccl.ccl_all_reduce_rmsnorm(x_n, y_n, P, rows, hidden, gamma, 1e-6,
                                                  ccl.CCL_BFLOAT16, stream, wt))
             ccl.check(ccl.ccl_reshard_copy(plan, src, dst, stream, wt))
             ccl.check(ccl.ccl_reshard_copy_fp8(plan, src, codes, scales, stream, wt))
 
-        _check_replays(calls, x_ar + x_ag + x_n + [gamma] + src,
-                       y_ar + y_ag + y_n + dst + codes + scales)
+        _check_replays(calls, x_ar + x_2 + x_ag + x_n + [gamma] + src,
+                       y_ar + y_lds + y_2 + y_ag + y_n + dst + codes + scales)
     finally:
         torch.cuda.synchronize()
         ccl.check(ccl.ccl_plan_destroy(plan))
