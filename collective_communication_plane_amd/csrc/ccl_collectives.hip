@@ -116,7 +116,12 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   //  - 6 <= P <= 16 from 512 MiB per rank, when every input starts at the same
   //    offset modulo 2 MiB (what separate framework allocations give): 16 KiB
   //    chunks, <= 3 WGs per CU (+1-19 %).  Inputs staggered against each
-  //    other keep 4 KiB chunks, where 16 KiB ones lose 12-15 %.
+  //    other keep 4 KiB chunks, where 16 KiB ones lose 12-15 %.  At P = 5 the
+  //    same inputs take 8 KiB chunks, <= 3 WGs per CU, the shape P = 3, 4
+  //    write through with anyway: over two sets of nine random placements
+  //    +4.3 and +4.7 % on average (+2 to +17 % at 512 MiB, within -3.1 to
+  //    +7 % at 768 MiB-1 GiB), where 16 KiB chunks averaged -0.6 to -3.5 %;
+  //    it loses 3-7 % at 384 MiB and 6 % on staggered inputs.
   const uint64_t per_rank = M * esz;
   if (d.kind == KIND_AR && !realign && l.stages <= 1 && !l.chunk_set && !l.occupancy_set &&
       !l.unroll_set) {
@@ -132,6 +137,9 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
       unroll = 1;
     } else if (d.P >= 6 && per_rank >= (uint64_t(512) << 20) && congruent) {
       chunk_bytes = 16384;
+      occupancy = 3;
+    } else if (d.P == 5 && per_rank >= (uint64_t(512) << 20) && congruent) {
+      chunk_bytes = 8192;
       occupancy = 3;
     }
   }

@@ -89,10 +89,11 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   write-through stores: 8 KiB chunks, <= 3 WGs per CU);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but
  *                   3 <= P <= 8 with 1-128 MiB per rank: 8 KiB chunks,
- *                   unroll 2, <= 4 WGs per CU; and 6 <= P <= 16 from 512 MiB
- *                   per rank when every input starts at the same offset
- *                   modulo 2 MiB (separate framework allocations): 16 KiB
- *                   chunks, <= 3 WGs per CU
+ *                   unroll 2, <= 4 WGs per CU; and from 512 MiB per rank
+ *                   when every input starts at the same offset modulo 2 MiB
+ *                   (separate framework allocations): 16 KiB chunks, <= 3
+ *                   WGs per CU at 6 <= P <= 16, 8 KiB chunks, <= 3 WGs per
+ *                   CU at P = 5
  *   reduce-scatter and reduce  register-direct, 8 KiB chunks, unroll 2,
  *                   <= 4 (P <= 2) or 3 WGs per CU, but 4 KiB chunks, unroll 1,
  *                   <= 4 WGs per CU for 9 <= P <= 12

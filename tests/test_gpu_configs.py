@@ -274,6 +274,7 @@ RULE_CASES = [
     (12, 32, "bf16", "max", "the same at P = 12"),
     (16, 64, "bf16", "sum", "the same at P = 16"),
     (6, 512, "bf16", "sum", "congruent inputs from 512 MiB: 16 KiB chunks, write-through"),
+    (5, 512, "f32", "max", "the same at P = 5: 8 KiB chunks, write-through"),
 ]
 
 
