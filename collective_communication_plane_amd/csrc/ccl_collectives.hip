@@ -123,11 +123,11 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   //    +7 % at 768 MiB-1 GiB), where 16 KiB chunks averaged -0.6 to -3.5 %;
   //    it loses 3-7 % at 384 MiB and 6 % on staggered inputs.
   const uint64_t per_rank = M * esz;
+  bool congruent = true;  // every input at one offset modulo 2 MiB
+  for (int r = 1; r < ni; ++r)
+    congruent = congruent && ((uintptr_t)a.in[r] - (uintptr_t)a.in[0]) % (uint64_t(2) << 20) == 0;
   if (d.kind == KIND_AR && !realign && l.stages <= 1 && !l.chunk_set && !l.occupancy_set &&
       !l.unroll_set) {
-    bool congruent = true;
-    for (int r = 1; r < d.P; ++r)
-      congruent = congruent && ((uintptr_t)a.in[r] - (uintptr_t)a.in[0]) % (uint64_t(2) << 20) == 0;
     if (d.P >= 3 && d.P <= 8 && per_rank >= (uint64_t(1) << 20) &&
         per_rank <= (uint64_t(128) << 20)) {
       chunk_bytes = 8192;
@@ -202,15 +202,19 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // <= 6 WGs per CU, +0.1-9 % over 8 KiB / unroll 2 / <= 3 in all 18 cells at
   // 288 MiB-1 GiB (<= 4, 5, 7, 8 or uncapped trail <= 6); P = 3, 4 with 8 KiB
   // chunks and <= 3 WGs per CU (P = 4 at 256 MiB-1 GiB: the other shapes
-  // tried within 1.2 % of it or behind, by up to 13 %).  P = 1 has
-  // write-through only when asked for and keeps its own shape (the <= 3 cap
-  // halves a copy's rate there).
+  // tried within 1.2 % of it or behind, by up to 13 %), except at P = 4 from
+  // 512 MiB per rank on inputs staggered against each other, where 4 KiB
+  // chunks won all 12 cells of four stagger gaps at 512 MiB-1 GiB by 2.5-8.5 %
+  // (at 384 MiB they lose 3-7 %; on congruent inputs 8 %; at P = 3 10 % on
+  // both).  P = 1 has write-through only when asked for and keeps its own
+  // shape (the <= 3 cap halves a copy's rate there).
   if (wt && d.kind == KIND_AR && d.P == 2) {
     if (!l.chunk_set) chunk_bytes = 4096;
     if (!l.unroll_set) unroll = 1;
     if (!l.occupancy_set) occupancy = 6;
   } else if (wt && d.kind == KIND_AR && d.P >= 3 && d.P <= 4) {
-    if (!l.chunk_set) chunk_bytes = 8192;
+    const bool staggered_big = d.P == 4 && !congruent && per_rank >= (uint64_t(512) << 20);
+    if (!l.chunk_set) chunk_bytes = staggered_big ? 4096 : 8192;
     if (!l.occupancy_set) occupancy = 3;
   }
   p.occupancy = occupancy;

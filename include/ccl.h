@@ -86,7 +86,9 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                   write-through stores 4 KiB chunks, unroll 1, <= 6 WGs
  *                   per CU;
  *                   P = 3, 4: 4 KiB chunks, unroll 1, <= 6 WGs per CU (with
- *                   write-through stores: 8 KiB chunks, <= 3 WGs per CU);
+ *                   write-through stores: 8 KiB chunks, <= 3 WGs per CU, but
+ *                   4 KiB chunks at P = 4 from 512 MiB per rank when the
+ *                   inputs do not all start at one offset modulo 2 MiB);
  *                   P >= 5: 4 KiB chunks, unroll 1, <= 3 WGs per CU; but
  *                   3 <= P <= 8 with 1-128 MiB per rank: 8 KiB chunks,
  *                   unroll 2, <= 4 WGs per CU; and from 512 MiB per rank

@@ -318,6 +318,46 @@ def test_ar_write_through_shapes_with_a_ragged_tail(P, mib):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("P, mib", [(4, 512), (5, 512)])
+def test_ar_staggered_inputs_from_512mib(P, mib):
+    """Inputs staggered against each other (one allocation, 2 MiB + 4 KiB
+    apart), where the congruence test picks other chunk sizes than for
+    separate allocations: 4 KiB chunks at P = 4 (instead of 8 KiB) and at
+    P = 5 (instead of 8 KiB for congruent inputs).  The default launch equals
+    both forced shapes byte for byte, and sampled points equal the oracle."""
+    import bench
+
+    n = (mib << 20) // 4 + 3  # fp32, a count 3 past whole vectors
+    print(f"AR staggered, P={P}, n={n} f32", flush=True)
+    dx, _ = bench.rank_slab(P, 4 * n, DEV)
+    src = si.device_rank_buffers(P, n, "f32", "normal", seed=60 + P, device=DEV)
+    for d, t in zip(dx, src):
+        d.copy_(t.view(torch.uint8))
+    del src
+    xs = [d.view(torch.float32) for d in dx]
+    outs = {}
+    stream = torch.cuda.current_stream()
+    for name, cfg in (("default", None),
+                      ("4K", ccl.LaunchConfig(chunk_bytes=4096, unroll=1, occupancy=3)),
+                      ("8K", ccl.LaunchConfig(chunk_bytes=8192, unroll=1, occupancy=3))):
+        ys, _ = bench.rank_slab(P, 4 * n, DEV)
+        outs[name] = [y.view(torch.float32) for y in ys]
+        ccl.check(ccl.ccl_all_reduce(xs, outs[name], P, n, ccl.CCL_FLOAT32, ccl.CCL_SUM, stream,
+                                     cfg))
+    torch.cuda.synchronize()
+    for name in ("4K", "8K"):
+        for q in range(P):
+            assert torch.equal(outs[name][q].view(torch.int32),
+                               outs["default"][q].view(torch.int32)), (name, q)
+    idx = si.sample_indices(n, 50_000, seed=P)
+    xin = gather_at(xs, idx, "f32")
+    want = oracle.fold_at(xin, "f32", "sum", np.arange(idx.size, dtype=np.uint64))
+    got = gather_at([outs["default"][P - 1]], idx, "f32")[0]
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+    del dx, xs, outs
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("P", [13, 16])
 def test_ag_write_through_up_to_p16(P):
     """All-gather at P = 13 and 16 with 256 MiB of input in all (write-through
