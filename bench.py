@@ -861,6 +861,15 @@ def defaults(dev, stream) -> None:
         ms = timed(fn, steps, 3, stream, 0.03)
         return nbytes / (ms * 1e-3) / 1e9
 
+    def both_ways(fns, nbytes, steps=20):
+        """GB/s of each callable, timed once in order and once in reverse order
+        and averaged: a cell's place in its row otherwise biases it (the first
+        cells timed on fresh buffers or a fresh plan read up to a few per cent
+        low)."""
+        fwd = [gbs(f, nbytes, steps) for f in fns]
+        rev = [gbs(f, nbytes, steps) for f in reversed(fns)][::-1]
+        return [(a + b) / 2 for a, b in zip(fwd, rev)]
+
     def table(title, header):
         """A markdown table whose rows are printed as they are measured."""
         print(f"\n### {title}\n", flush=True)
@@ -895,10 +904,10 @@ def defaults(dev, stream) -> None:
                 for b in x:
                     b.view(torch.bfloat16).uniform_(-1, 1)
                 n = per_rank // 2
-                vals = [gbs(lambda: ccl.check(ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16,
-                                                                 ccl.CCL_SUM, stream, c)),
-                            2 * P * per_rank) for _, c in shapes]
-                row([P, per_rank >> 20, layout, *vals])
+                fns = [lambda c=c: ccl.check(ccl.ccl_all_reduce(x, y, P, n, ccl.CCL_BFLOAT16,
+                                                                ccl.CCL_SUM, stream, c))
+                       for _, c in shapes]
+                row([P, per_rank >> 20, layout, *both_ways(fns, 2 * P * per_rank)])
                 del x, y
                 torch.cuda.empty_cache()
 
@@ -925,10 +934,11 @@ def defaults(dev, stream) -> None:
         y = [b[off:off + m * 2] for b in yb]
         for b in x:
             b.view(torch.bfloat16).uniform_(-1, 1)
-        vals = [gbs(lambda: ccl.check(ccl.ccl_reduce_scatter(x, y, P, m, ccl.CCL_BFLOAT16,
-                                                             ccl.CCL_SUM, stream, c)),
-                    P * P * m * 2 + P * m * 2) for _, c in shapes]
-        row([P, f"{m * 2 / 2**20:.1f}", "no" if off else "yes", *vals])
+        fns = [lambda c=c: ccl.check(ccl.ccl_reduce_scatter(x, y, P, m, ccl.CCL_BFLOAT16,
+                                                            ccl.CCL_SUM, stream, c))
+               for _, c in shapes]
+        row([P, f"{m * 2 / 2**20:.1f}", "no" if off else "yes",
+             *both_ways(fns, P * P * m * 2 + P * m * 2)])
         del x, y, yb
         torch.cuda.empty_cache()
 
@@ -939,31 +949,32 @@ def defaults(dev, stream) -> None:
         for total in (64 << 20, 256 << 20):
             M = total // P // 2 // 128 * 128
             sets = [(bufs(P, M * 2, "alloc"), bufs(P, P * M * 2, "alloc")) for _ in range(3)]
-            vals = []
-            for c in (None, L(store_policy=1), L(store_policy=2)):
+
+            def make_ag(c):
                 k = [0]
 
                 def ag():
                     x, y = sets[k[0] % 3]
                     k[0] += 1
                     ccl.check(ccl.ccl_all_gather(x, y, P, M, ccl.CCL_BFLOAT16, stream, c))
-                vals.append(gbs(ag, P * M * 2 * (1 + P), 24))
-            row([P, P * M * 2 >> 20, *vals])
+                return ag
+            fns = [make_ag(c) for c in (None, L(store_policy=1), L(store_policy=2))]
+            row([P, P * M * 2 >> 20, *both_ways(fns, P * M * 2 * (1 + P), 24)])
             del sets
             torch.cuda.empty_cache()
     P, n = 8, (256 << 20) // 2
     sets = [(torch.empty(2 * n, dtype=torch.uint8, device=dev), bufs(P, 2 * n, "alloc"))
             for _ in range(3)]
-    vals = []
-    for c in (None, L(store_policy=1), L(store_policy=2)):
+    def make_bc(c):
         k = [0]
 
         def bc():
             x, y = sets[k[0] % 3]
             k[0] += 1
             ccl.check(ccl.ccl_broadcast(x, y, P, n, ccl.CCL_BFLOAT16, 0, stream, c))
-        vals.append(gbs(bc, 2 * n * (P + 1), 24))
-    row(["8 (broadcast)", 256, *vals])
+        return bc
+    fns = [make_bc(c) for c in (None, L(store_policy=1), L(store_policy=2))]
+    row(["8 (broadcast)", 256, *both_ways(fns, 2 * n * (P + 1), 24)])
     del sets
     torch.cuda.empty_cache()
 
@@ -981,15 +992,14 @@ def defaults(dev, stream) -> None:
             for b in x:
                 b.view(torch.bfloat16).normal_()
             g = torch.empty(hidden, dtype=torch.bfloat16, device=dev).uniform_(-1, 1)
-            vals = []
-            for name, c in shapes:
-                if name == "split rows" and row_bytes <= 4096:
-                    vals.append("-")
-                    continue
-                vals.append(gbs(lambda: ccl.check(ccl.ccl_all_reduce_rmsnorm(
-                    x, y, P, rows_n, hidden, g, 1e-6, ccl.CCL_BFLOAT16, stream, c)),
-                    2 * P * rows_n * row_bytes + row_bytes))
-            row([P, row_bytes >> 10, *vals])
+            live = [(name, c) for name, c in shapes
+                    if not (name == "split rows" and row_bytes <= 4096)]
+            fns = [lambda c=c: ccl.check(ccl.ccl_all_reduce_rmsnorm(
+                x, y, P, rows_n, hidden, g, 1e-6, ccl.CCL_BFLOAT16, stream, c))
+                for _, c in live]
+            got = dict(zip([name for name, _ in live],
+                           both_ways(fns, 2 * P * rows_n * row_bytes + row_bytes)))
+            row([P, row_bytes >> 10, *[got.get(name, "-") for name, _ in shapes]])
             del x, y
             torch.cuda.empty_cache()
 
@@ -1024,9 +1034,9 @@ def defaults(dev, stream) -> None:
         for b in dsrc:
             b.view(torch.bfloat16).normal_()
         ddst = [torch.empty(tb * rho // n_dst, dtype=torch.uint8, device=dev) for _ in range(n_dst)]
-        vals = [gbs(lambda: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream, c)),
-                    tb * (1 + rho)) for _, c in shapes]
-        row([name, rho, *vals])
+        fns = [lambda c=c: ccl.check(ccl.ccl_reshard_copy(plan, dsrc, ddst, stream, c))
+               for _, c in shapes]
+        row([name, rho, *both_ways(fns, tb * (1 + rho))])
         ccl.check(ccl.ccl_plan_destroy(plan))
         del dsrc, ddst
         torch.cuda.empty_cache()
