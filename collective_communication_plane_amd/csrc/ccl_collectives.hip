@@ -169,13 +169,15 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // and write-through gains up to 30 % more; with 341-512 MiB of input it
   // loses 2-6 %, at P = 3 it loses, with 3 workgroups per CU up to 30 %.)  The
   // all-reduce, past the range of the 8 KiB / unroll-2 shape above: at P = 2
-  // above 256 MiB per rank (+1-6 % at 384 MiB to 1 GiB), at 3 <= P <= 6 from
-  // 256 MiB (P = 4 at 256 MiB: +19-22 % before the input-0 cacheable stream,
-  // level after it; P = 3-6 with 341-682 MiB per rank: +2-11 %, P = 3, 4 with
-  // 8 KiB chunks and <= 3 workgroups per CU; P = 3 loses 3-6 % at
-  // 128-192 MiB), at P = 7, 8 above 128 MiB (+2-11 % at 136 MiB to 1 GiB,
-  // +3-4 % at the P = 8 x 256 MiB point), and at 9 <= P <= 16 from 16 MiB
-  // (+0.5-8 % at 16-256 MiB and up to 1 GiB, one cell at -0.1 %).  Only
+  // above 256 MiB per rank (+1-6 % at 384 MiB to 1 GiB), at P = 3 from
+  // 256 MiB (P = 3-6 with 341-682 MiB per rank: +2-11 %, P = 3, 4 with 8 KiB
+  // chunks and <= 3 workgroups per CU; P = 3 loses 3-6 % at 128-192 MiB), at
+  // 4 <= P <= 8 above 128 MiB (P = 4-6 at 144-224 MiB: +1.6 to +2.8 % on
+  // average over both layouts on two boxes, -1.3 to +12 % per cell, and at
+  // 192 MiB +1-8 % in five runs of the defaults table; P = 7, 8: +2-11 % at
+  // 136 MiB to 1 GiB, +3-4 % at the P = 8 x 256 MiB point), and at
+  // 9 <= P <= 16 from 16 MiB (+0.5-8 % at 16-256 MiB and up to 1 GiB, one
+  // cell at -0.1 %).  Only
   // where every chunk's stores
   // start on a 256-byte boundary: the all-gather at P = 8 with shards of
   // 2^24 + 8 elements ran 4086 GB/s with them against 5166 without, and every
@@ -183,7 +185,7 @@ ccl_status_t launch_collective(const CollDesc &d, const Launch &l, hipStream_t s
   // address a chunk through a buffer resource with 31-bit offsets.
   const uint64_t ag_in_bytes = (uint64_t)(d.single ? 1 : d.P) * M * esz;
   const uint64_t ar_wt_from = d.P == 2   ? (uint64_t(256) << 20) + 1
-                              : d.P <= 6  ? (uint64_t(256) << 20)
+                              : d.P == 3  ? (uint64_t(256) << 20)
                               : d.P <= 8  ? (uint64_t(128) << 20) + 1
                                           : (uint64_t(16) << 20);
   bool wt = l.store_wt;

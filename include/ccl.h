@@ -186,7 +186,7 @@ typedef enum { CCL_SUM = 0, CCL_MIN = 1, CCL_MAX = 2 } ccl_op_t;
  *                RMSNorm, for chunks of up to 1 GiB), 2 = nontemporal only,
  *                0 = default:
  *                write-through for the all-reduce at P = 2 above 256 MiB
- *                per rank, at 3 <= P <= 6 from 256 MiB, at P = 7, 8 above
+ *                per rank, at P = 3 from 256 MiB, at 4 <= P <= 8 above
  *                128 MiB and at 9 <= P <= 16 from 16 MiB, for
  *                reduce-scatter and reduce at P <= 8, for
  *                all-gather and broadcast at P = 2, at 7 <= P <= 16 with at

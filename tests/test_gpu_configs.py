@@ -269,6 +269,8 @@ RULE_CASES = [
     (3, 64, "f32", "min", "3 <= P <= 8 up to 128 MiB: 8 KiB chunks, unroll 2"),
     (5, 128, "bf16", "sum", "the same at its upper bound"),
     (7, 160, "bf16", "sum", "P = 7 above 128 MiB: write-through"),
+    (4, 144, "bf16", "min", "P = 4 above 128 MiB: write-through, 8 KiB chunks"),
+    (6, 160, "f32", "sum", "P = 6 above 128 MiB: write-through"),
     (8, 136, "bf16", "min", "P = 8 above 128 MiB: write-through"),
     (9, 16, "f32", "sum", "P >= 9 from 16 MiB: write-through"),
     (12, 32, "bf16", "max", "the same at P = 12"),
