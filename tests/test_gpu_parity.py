@@ -163,6 +163,12 @@ def test_launch_config_does_not_change_results(cfg):
     got = run_ar(xf, "f32", "sum", cfg=ccl.LaunchConfig(**cfg))
     for q in range(P):
         np.testing.assert_array_equal(got[q].view(np.uint32), want[q].view(np.uint32))
+    # fp16, max (its own kernel instantiations)
+    xh = si.rank_buffers(P, n, "f16", "normal", seed=9)
+    want = oracle.all_reduce(xh, "f16", "max")
+    got = run_ar(xh, "f16", "max", cfg=ccl.LaunchConfig(**cfg))
+    for q in range(P):
+        np.testing.assert_array_equal(got[q], want[q])
     # reduce-scatter and all-gather under the same config
     m = n // P + 3
     xr = si.rank_buffers(P, P * m, "f32", "uniform", seed=6)
