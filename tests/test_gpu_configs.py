@@ -290,10 +290,10 @@ def test_ar_default_rule_branches(P, mib, dtype, op, branch):
     _ar_sampled(dx, P, n, dtype, op)
 
 
-@pytest.mark.parametrize("P, mib", [(2, 288), (4, 256), (8, 136)])
+@pytest.mark.parametrize("P, mib", [(2, 288), (4, 144), (4, 256), (8, 136), (12, 20), (16, 17)])
 def test_ar_write_through_shapes_with_a_ragged_tail(P, mib):
     """The all-reduce's write-through shapes (P = 2: 4 KiB chunks, unroll 1;
-    P = 4: 8 KiB chunks; P = 8: 4 KiB chunks) on a count 5 elements past whole
+    P = 4: 8 KiB chunks; P >= 5: 4 KiB chunks) on a count 5 elements past whole
     vectors, so the last chunk is partial and a scalar tail follows it.  Every
     output equals the nontemporal-only launch (store_policy = 2) byte for byte,
     and sampled points, the last 4096 elements among them, equal the oracle."""
